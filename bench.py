@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE dispatch -> combine hot path on one MI355X.
+
+One step = the whole path on one batch: moe_dispatch_layout (counts, padded
+prefix, stable ranks) -> moe_dispatch (bf16 scatter into the
+expert-contiguous, 128-row-padded buffer) -> moe_combine (weighted gather-sum
++ shared row).  Inputs are seeded synthetic tensors already resident in HBM
+when the timed region starts.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload skewed]
+
+`value` is algorithmic bytes per step (real rows only, never padding) divided
+by the measured step time, in GB/s; `tokens_per_s` is tokens per step over the
+same time.  The `roofline` object covers the kernel that moves the most bytes
+(combine): its algorithmic bytes per launch over its mean launch time measured
+with HIP events on the launch stream inside the timed region.  `cpu_baseline`
+times the CPU oracle (single-threaded C) on the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
+METRIC = "dispatch+combine achieved HBM GB/s and tokens/s, H=7168 E=256 K=8 bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_bf16_skewed_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "combine_moe_dispatch_layout_amd", "csrc", f)
+                  for f in ("combine.hip", "moe_internal.h")]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="skewed",
+                   choices=["tiny", "decode", "skewed", "fp8", "large"])
+    p.add_argument("--sets", type=int, default=0,
+                   help="buffer sets rotated across steps (0 = enough to exceed 2 GiB)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="run only a plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------- byte model
+
+def algorithmic_bytes(bs, h, e, k, shared=True, fp8=False):
+    """Bytes each kernel must move: real rows only, metadata once per kernel."""
+    layout = 4 * bs * k + 4 * bs * k + 4 * e + 4 * (e + 1)
+    if fp8:
+        dispatch = 2 * bs * h + bs * k * (h + 4 * (h // 128)) + 8 * bs * k + 4 * (e + 1)
+    else:
+        dispatch = 2 * bs * h + 2 * bs * k * h + 8 * bs * k + 4 * (e + 1)
+    combine = (2 * bs * k * h + (2 * bs * h if shared else 0) + 2 * bs * h + 12 * bs * k
+               + 4 * (e + 1))
+    return {"layout": layout, "dispatch": dispatch, "combine": combine}
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per combine launch from the committed counter summary, or
+    None when it is missing or the kernel source changed since."""
+    if workload != "skewed" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"^source_hash:\s*(\w+)", txt, re.M)
+    m_bytes = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(KERNEL_SOURCES):
+        return None
+    return float(m_bytes.group(1))
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(w, budget_s):
+    """The oracle as it stands (single-threaded C, gcc -O2), timed on this
+    host over whole passes of the workload until the budget is spent."""
+    import numpy as np
+    import oracle
+    import workloads
+
+    cap = oracle.capacity(w.bs, w.topk, w.experts, w.align)
+    inp = workloads.make(w, rows_y=cap)
+    ids, sc = inp["expert_ids"], inp["expert_scales"]
+    x = workloads.bits(inp["x"])
+    y = workloads.bits(inp["y"])
+    sh = None if inp["shared"] is None else workloads.bits(inp["shared"])
+    out = np.full((cap, w.hidden), oracle.SENTINEL_BF16, np.uint16)  # pages touched up front
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        c, s, r, _ = oracle.layout(ids, w.experts, w.align)
+        oracle.dispatch_bf16(x, ids, r, s, w.experts, cap, out=out)
+        oracle.combine(y, ids, r, s, sc, sh, w.experts)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= budget_s and len(times) >= 2:
+            break
+    t = sorted(times)[len(times) // 2]
+    b = sum(algorithmic_bytes(w.bs, w.hidden, w.experts, w.topk, sh is not None).values())
+    return {"value": round(b / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_per_s": round(w.bs / t, 1), "ms_per_pass": round(t * 1e3, 2),
+            "sample": f"whole {w.name} batch ({w.bs} tokens: layout + bf16 dispatch + "
+                      f"combine), {len(times)} passes in {time.perf_counter() - t_start:.1f} s, "
+                      "median pass, single thread"}
+
+
+# ---------------------------------------------------------------- GPU run
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the path is single-device; no collectives are built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import combine_moe_dispatch_layout_amd as moe
+    import workloads
+
+    moe.load_library()
+    w = workloads.WORKLOADS[args.workload]
+    if w.fp8:
+        raise SystemExit("the bench line times the bf16 path; use the parity tests for fp8")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cap = moe.moe_dispatch_capacity(w.bs, w.topk, w.experts, w.align)
+    inp = workloads.make(w, rows_y=None if w.identity_experts else cap)
+
+    nbytes = algorithmic_bytes(w.bs, w.hidden, w.experts, w.topk, inp["shared"] is not None)
+    step_bytes = sum(nbytes.values())
+    sets = args.sets or max(1, min(64, -(-(2 << 30) // step_bytes)))
+
+    ids = torch.from_numpy(inp["expert_ids"]).to(dev)
+    scales = torch.from_numpy(inp["expert_scales"]).to(dev)
+    x0 = inp["x"].to(dev)
+    y0 = None if w.identity_experts else inp["y"].to(dev)
+    sh0 = None if inp["shared"] is None else inp["shared"].to(dev)
+    bufs = []
+    for i in range(sets):
+        ex = torch.empty((cap, w.hidden), dtype=torch.bfloat16, device=dev)
+        bufs.append({
+            "x": x0 if i == 0 else x0.clone(),
+            "y": ex if y0 is None else (y0 if i == 0 else y0.clone()),
+            "shared": None if sh0 is None else (sh0 if i == 0 else sh0.clone()),
+            "expand_x": ex,
+            "out": torch.empty((w.bs, w.hidden), dtype=torch.bfloat16, device=dev),
+            "layout": moe.Layout(torch.empty(w.experts, dtype=torch.int32, device=dev),
+                                 torch.empty(w.experts + 1, dtype=torch.int32, device=dev),
+                                 torch.empty(w.bs * w.topk, dtype=torch.int32, device=dev),
+                                 torch.empty(1, dtype=torch.int32, device=dev)),
+        })
+    ws_bytes = moe.moe_dispatch_layout_workspace_size(w.bs, w.topk, w.experts)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(b, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        lay = moe.moe_dispatch_layout(ids, w.experts, w.align, out=b["layout"], workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        moe.moe_dispatch(b["x"], ids, lay.expand_idx, lay.ep_send_counts, w.experts,
+                         expand_x=b["expand_x"], capacity_rows=cap)
+        if ev is not None:
+            ev[2].record(stream)
+        moe.moe_combine(b["y"], ids, lay.expand_idx, lay.ep_send_counts, scales, b["shared"],
+                        w.experts, out=b["out"])
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(bufs[i % sets])
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(bufs[i % sets], events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    lay_ms = [e[0].elapsed_time(e[1]) for e in events]
+    dis_ms = [e[1].elapsed_time(e[2]) for e in events]
+    com_ms = [e[2].elapsed_time(e[3]) for e in events]
+    gpu_ms = [e[0].elapsed_time(e[3]) for e in events]
+    mean = lambda v: sum(v) / len(v)
+    ms_per_step = elapsed * 1e3 / args.steps
+    status = int(bufs[0]["layout"].status.cpu()[0])
+    if status != 0:
+        raise SystemExit(f"layout status flags {status}: routing is invalid")
+
+    combine_s = mean(com_ms) / 1e3
+    achieved = nbytes["combine"] / combine_s / 1e9
+    traffic = read_traffic(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms_per_step / 1e3) / 1e9, 2),
+        "unit": "GB/s",
+        "tokens_per_s": round(w.bs / (ms_per_step / 1e3), 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded generators; no routing trace or trained weights)",
+        "config": {"workload": w.name, "bs": w.bs, "hidden": w.hidden, "experts": w.experts,
+                   "topk": w.topk, "routing": w.routing + (f"(alpha={w.alpha})"
+                                                           if w.routing == "zipf" else ""),
+                   "align": w.align, "capacity_rows": cap, "buffer_sets": sets,
+                   "bytes_per_step": step_bytes},
+        "kernels_ms": {"layout": round(mean(lay_ms), 4), "dispatch": round(mean(dis_ms), 4),
+                       "combine": round(mean(com_ms), 4), "step_gpu": round(mean(gpu_ms), 4)},
+        "kernels_gbs": {"layout": round(nbytes["layout"] / mean(lay_ms) / 1e6, 1),
+                        "dispatch": round(nbytes["dispatch"] / mean(dis_ms) / 1e6, 1),
+                        "combine": round(achieved, 1)},
+        "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": nbytes["combine"]},
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,217 @@
+"""MI355X (gfx950) MoE token dispatch / combine.
+
+A thin Python binding over ``libmoe_dispatch.so`` (C ABI in
+``include/moe_dispatch.h``).  Every step of the path runs in the library's HIP
+kernels; this module only marshals torch tensors (device memory and the
+current stream) into pointers.  If the library is not built the import of the
+entry points fails loudly -- there is no fallback.
+
+Entry points (same names as the C ABI):
+
+* ``moe_dispatch_layout(expert_ids, num_experts, align=128)`` ->
+  ``Layout(expert_counts, ep_send_counts, expand_idx, status)``
+* ``moe_dispatch(x, expert_ids, layout_or_arrays..., out_dtype="bf16")`` ->
+  ``expand_x`` (and ``quant_scales`` for e4m3)
+* ``moe_combine(expand_x, expert_ids, expand_idx, ep_send_counts,
+  expert_scales, shared_expert_x)`` -> ``x_out``
+* ``moe_dispatch_capacity`` / ``moe_dispatch_layout_workspace_size``
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+import torch
+
+__all__ = [
+    "MoeError", "Layout", "library_path", "load_library",
+    "moe_dispatch_capacity", "moe_dispatch_layout_workspace_size",
+    "moe_dispatch_layout", "moe_dispatch", "moe_combine",
+    "MOE_BF16", "MOE_FP8_E4M3", "MOE_FLAG_ID_RANGE", "MOE_FLAG_DUP_ID", "MOE_FLAG_GUARD",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmoe_dispatch.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = range(5)
+MOE_BF16, MOE_FP8_E4M3 = 0, 1
+MOE_FLAG_ID_RANGE, MOE_FLAG_DUP_ID, MOE_FLAG_GUARD = 1, 2, 4
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (status {code})")
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with "
+            "`python -m combine_moe_dispatch_layout_amd.build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sigs = {
+        "moe_abi_version": (ctypes.c_int, []),
+        "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_dispatch_capacity": (i64, [i32, i32, i32, i32]),
+        "moe_dispatch_layout_workspace_size": (sz, [i32, i32, i32]),
+        "moe_dispatch_layout": (ctypes.c_int, [P, i32, i32, i32, i32, P, P, P, P, P, sz, P]),
+        "moe_dispatch": (ctypes.c_int, [P, i64, i32, i32, P, P, P, i32, i32, P, i64, i64, i32,
+                                        P, P, P]),
+        "moe_combine": (ctypes.c_int, [P, i64, i64, P, P, P, P, P, i64, i32, i32, i32, i32, P,
+                                       P, P]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != MOE_OK:
+        raise MoeError(rc, load_library().moe_status_string(rc).decode())
+
+
+def _stream(t: torch.Tensor) -> Optional[int]:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str, contiguous: bool = True) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _row_stride(t: torch.Tensor, name: str) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return t.stride(0)
+
+
+class Layout(NamedTuple):
+    expert_counts: torch.Tensor   # int32 [E]
+    ep_send_counts: torch.Tensor  # int32 [E+1], exclusive padded prefix, last = M_pad
+    expand_idx: torch.Tensor      # int32 [BS*K], within-expert rank (-1 = dropped pair)
+    status: torch.Tensor          # int32 [1], moe_flag bits
+
+
+def moe_dispatch_capacity(bs: int, k: int, num_experts: int, align: int = 128) -> int:
+    cap = load_library().moe_dispatch_capacity(bs, k, num_experts, align)
+    if cap < 0:
+        raise MoeError(MOE_ERR_INVALID_ARG, "invalid layout arguments")
+    return int(cap)
+
+
+def moe_dispatch_layout_workspace_size(bs: int, k: int, num_experts: int) -> int:
+    return int(load_library().moe_dispatch_layout_workspace_size(bs, k, num_experts))
+
+
+def moe_dispatch_layout(expert_ids: torch.Tensor, num_experts: int, align: int = 128, *,
+                        out: Optional[Layout] = None,
+                        workspace: Optional[torch.Tensor] = None) -> Layout:
+    """Counts, padded prefix and stable ranks of a [BS, K] int32 routing."""
+    _need(expert_ids, torch.int32, "expert_ids")
+    if expert_ids.dim() != 2:
+        raise ValueError("expert_ids must be [BS, K]")
+    bs, k = expert_ids.shape
+    dev = expert_ids.device
+    if out is None:
+        out = Layout(torch.empty(num_experts, dtype=torch.int32, device=dev),
+                     torch.empty(num_experts + 1, dtype=torch.int32, device=dev),
+                     torch.empty(bs * k, dtype=torch.int32, device=dev),
+                     torch.empty(1, dtype=torch.int32, device=dev))
+    ws_bytes = moe_dispatch_layout_workspace_size(bs, k, num_experts)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    rc = load_library().moe_dispatch_layout(
+        _ptr(expert_ids), bs, k, num_experts, align, _ptr(out.expert_counts),
+        _ptr(out.ep_send_counts), _ptr(out.expand_idx), _ptr(out.status), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(expert_ids))
+    _check(rc)
+    return out
+
+
+def moe_dispatch(x: torch.Tensor, expert_ids: torch.Tensor, expand_idx: torch.Tensor,
+                 ep_send_counts: torch.Tensor, num_experts: int, *,
+                 capacity_rows: Optional[int] = None, out_dtype: str = "bf16",
+                 expand_x: Optional[torch.Tensor] = None,
+                 quant_scales: Optional[torch.Tensor] = None,
+                 status: Optional[torch.Tensor] = None, align: int = 128):
+    """Scatter x [BS, H] bf16 into expand_x [capacity_rows, H] (bf16, or e4m3
+    codes as uint8 plus fp32 scales [capacity_rows, H/128]).  Returns
+    ``expand_x`` or ``(expand_x, quant_scales)``."""
+    _need(x, torch.bfloat16, "x", contiguous=False)
+    _need(expert_ids, torch.int32, "expert_ids")
+    _need(expand_idx, torch.int32, "expand_idx")
+    _need(ep_send_counts, torch.int32, "ep_send_counts")
+    bs, hidden = x.shape
+    k = expert_ids.shape[1]
+    dtype = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "e4m3": MOE_FP8_E4M3}[out_dtype]
+    if capacity_rows is None:
+        capacity_rows = (expand_x.shape[0] if expand_x is not None
+                         else moe_dispatch_capacity(bs, k, num_experts, align))
+    if expand_x is None:
+        expand_x = torch.empty((capacity_rows, hidden),
+                               dtype=torch.bfloat16 if dtype == MOE_BF16 else torch.uint8,
+                               device=x.device)
+    if dtype == MOE_FP8_E4M3 and quant_scales is None:
+        quant_scales = torch.empty((capacity_rows, hidden // 128), dtype=torch.float32,
+                                   device=x.device)
+    rc = load_library().moe_dispatch(
+        _ptr(x), _row_stride(x, "x"), bs, hidden, _ptr(expert_ids), _ptr(expand_idx),
+        _ptr(ep_send_counts), k, num_experts, _ptr(expand_x), _row_stride(expand_x, "expand_x"),
+        capacity_rows, dtype, _ptr(quant_scales) if dtype == MOE_FP8_E4M3 else None,
+        _ptr(status), _stream(x))
+    _check(rc)
+    return expand_x if dtype == MOE_BF16 else (expand_x, quant_scales)
+
+
+def moe_combine(expand_x: torch.Tensor, expert_ids: torch.Tensor, expand_idx: torch.Tensor,
+                ep_send_counts: torch.Tensor, expert_scales: torch.Tensor,
+                shared_expert_x: Optional[torch.Tensor], num_experts: int, *,
+                out: Optional[torch.Tensor] = None,
+                status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x_out[t] = sum_j expert_scales[t,j] * expand_x[slot(t,j)] + shared_expert_x[t]."""
+    _need(expand_x, torch.bfloat16, "expand_x", contiguous=False)
+    _need(expert_ids, torch.int32, "expert_ids")
+    _need(expand_idx, torch.int32, "expand_idx")
+    _need(ep_send_counts, torch.int32, "ep_send_counts")
+    _need(expert_scales, torch.float32, "expert_scales")
+    bs, k = expert_ids.shape
+    cap, hidden = expand_x.shape
+    shared_stride = 0
+    if shared_expert_x is not None:
+        _need(shared_expert_x, torch.bfloat16, "shared_expert_x", contiguous=False)
+        shared_stride = _row_stride(shared_expert_x, "shared_expert_x")
+    if out is None:
+        out = torch.empty((bs, hidden), dtype=torch.bfloat16, device=expand_x.device)
+    _need(out, torch.bfloat16, "out")
+    rc = load_library().moe_combine(
+        _ptr(expand_x), _row_stride(expand_x, "expand_x"), cap, _ptr(expert_ids),
+        _ptr(expand_idx), _ptr(ep_send_counts), _ptr(expert_scales), _ptr(shared_expert_x),
+        shared_stride, bs, hidden, k, num_experts, _ptr(out), _ptr(status), _stream(expand_x))
+    _check(rc)
+    return out

@@ -1,0 +1,146 @@
+// api.hip -- the C ABI declared in include/moe_dispatch.h: host-side argument
+// checks, workspace sizing and kernel launches.  No call allocates, keeps
+// state or synchronises.
+//
+// Argument rules (each failure returns MOE_ERR_INVALID_ARG and enqueues
+// nothing): the npu_moe_distribute_combine page gives 1 <= num_experts <= 512,
+// 0 < K <= num_experts with K at most 16 (its widest top-K limit), and H a
+// positive multiple of 32; the page's per-product caps (BS <= 256/512,
+// H <= 7168) are not adopted.  The library adds: bs >= 0, align a power of two
+// in [1, 1024], bs*k and the padded capacity at most 2^30 (so 32-bit pair
+// indices keep headroom), H <= 65536 (a
+// multiple of 128 for e4m3 output), 16-byte aligned row bases and strides.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool is_pow2(int32_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t capacity_rows_for(int32_t bs, int32_t k, int32_t num_experts, int32_t align) {
+  const int64_t n = (int64_t)bs * k;
+  const int64_t used = n < num_experts ? n : num_experts;
+  return (int64_t)align * ((n + (int64_t)(align - 1) * used) / align);
+}
+
+bool layout_args_ok(int32_t bs, int32_t k, int32_t num_experts, int32_t align) {
+  if (bs < 0) return false;
+  if (num_experts < 1 || num_experts > moe::kMaxExperts) return false;
+  if (k < 1 || k > moe::kMaxTopK || k > num_experts) return false;
+  if (!is_pow2(align) || align > 1024) return false;
+  if (capacity_rows_for(bs, k, num_experts, align) > moe::kMaxRows) return false;
+  return true;
+}
+
+// Row rules shared by dispatch and combine; elem = bytes per element.
+bool row_ok(const void* base, int64_t stride, int32_t hidden, int elem) {
+  if (base == nullptr || !aligned16(base)) return false;
+  if (stride < hidden || ((stride * elem) & 15) != 0) return false;
+  return true;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return kAbiVersion; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument (shape, range, pointer or alignment)";
+    case MOE_ERR_WORKSPACE: return "workspace smaller than moe_dispatch_layout_workspace_size";
+    case MOE_ERR_UNSUPPORTED: return "unsupported dtype";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int64_t moe_dispatch_capacity(int32_t bs, int32_t k, int32_t num_experts, int32_t align) {
+  if (!layout_args_ok(bs, k, num_experts, align)) return -1;
+  return capacity_rows_for(bs, k, num_experts, align);
+}
+
+size_t moe_dispatch_layout_workspace_size(int32_t bs, int32_t k, int32_t num_experts) {
+  if (!layout_args_ok(bs, k, num_experts, 1)) return 0;
+  return moe::layout_workspace_bytes(moe::plan_layout(bs, k), num_experts);
+}
+
+int moe_dispatch_layout(const int32_t* expert_ids, int32_t bs, int32_t k, int32_t num_experts,
+                        int32_t align, int32_t* expert_counts, int32_t* ep_send_counts,
+                        int32_t* expand_idx, int32_t* status, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!layout_args_ok(bs, k, num_experts, align)) return MOE_ERR_INVALID_ARG;
+  if (expert_counts == nullptr || ep_send_counts == nullptr) return MOE_ERR_INVALID_ARG;
+  if (bs > 0 && (expert_ids == nullptr || expand_idx == nullptr)) return MOE_ERR_INVALID_ARG;
+  const moe::LayoutPlan plan = moe::plan_layout(bs, k);
+  const size_t need = moe::layout_workspace_bytes(plan, num_experts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_layout(expert_ids, k, num_experts, align, plan, expert_counts,
+                                       ep_send_counts, expand_idx, status, workspace,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int moe_dispatch(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
+                 const int32_t* expert_ids, const int32_t* expand_idx,
+                 const int32_t* ep_send_counts, int32_t k, int32_t num_experts, void* expand_x,
+                 int64_t expand_x_stride, int64_t capacity_rows, int32_t out_dtype,
+                 float* quant_scales, int32_t* status, void* stream) {
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  if (!layout_args_ok(bs, k, num_experts, 1)) return MOE_ERR_INVALID_ARG;
+  if (hidden <= 0 || hidden % 32 != 0 || hidden > 65536) return MOE_ERR_INVALID_ARG;
+  if (out_dtype == MOE_FP8_E4M3 && hidden % 128 != 0) return MOE_ERR_INVALID_ARG;
+  if (capacity_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (bs == 0) return MOE_OK;
+  if (expert_ids == nullptr || expand_idx == nullptr || ep_send_counts == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!row_ok(x, x_stride, hidden, 2)) return MOE_ERR_INVALID_ARG;
+  const int out_elem = out_dtype == MOE_BF16 ? 2 : 1;
+  if (!row_ok(expand_x, expand_x_stride, hidden, out_elem)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (out_dtype == MOE_BF16)
+    return hip_status(moe::launch_dispatch_bf16(x, x_stride, bs, hidden, expert_ids, expand_idx,
+                                                ep_send_counts, k, num_experts, expand_x,
+                                                expand_x_stride, capacity_rows, status, s));
+  if (quant_scales == nullptr || (reinterpret_cast<uintptr_t>(quant_scales) & 3u) != 0)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_dispatch_fp8(x, x_stride, bs, hidden, expert_ids, expand_idx,
+                                             ep_send_counts, k, num_experts, expand_x,
+                                             expand_x_stride, capacity_rows, quant_scales,
+                                             status, s));
+}
+
+int moe_combine(const void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
+                const int32_t* expert_ids, const int32_t* expand_idx,
+                const int32_t* ep_send_counts, const float* expert_scales,
+                const void* shared_expert_x, int64_t shared_stride, int32_t bs, int32_t hidden,
+                int32_t k, int32_t num_experts, void* x_out, int32_t* status, void* stream) {
+  if (!layout_args_ok(bs, k, num_experts, 1)) return MOE_ERR_INVALID_ARG;
+  if (hidden <= 0 || hidden % 32 != 0 || hidden > 65536) return MOE_ERR_INVALID_ARG;
+  if (capacity_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (bs == 0) return MOE_OK;
+  if (expert_ids == nullptr || expand_idx == nullptr || ep_send_counts == nullptr ||
+      expert_scales == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (capacity_rows > 0 && !row_ok(expand_x, expand_x_stride, hidden, 2))
+    return MOE_ERR_INVALID_ARG;
+  if (shared_expert_x != nullptr && !row_ok(shared_expert_x, shared_stride, hidden, 2))
+    return MOE_ERR_INVALID_ARG;
+  if (!row_ok(x_out, hidden, hidden, 2)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine(expand_x, expand_x_stride, capacity_rows, expert_ids,
+                                        expand_idx, ep_send_counts, expert_scales,
+                                        shared_expert_x, shared_stride, bs, hidden, k,
+                                        num_experts, x_out, status,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,195 @@
+/*
+ * moe_dispatch.h -- C ABI of the MI355X (gfx950) MoE token dispatch / combine
+ * library (libmoe_dispatch.so).
+ *
+ * The three entry points are the local (one-device) stages of the pair of
+ * operators documented on the torch_npu API reference page for
+ * npu_moe_distribute_combine (Ascend): the dispatch side lays token rows out
+ * expert-contiguously and returns expand_idx and the send counts in
+ * prefix-sum form; the combine side "returns along the same path" and forms
+ * the weighted sum of the formula in that page's 计算公式 (formula) section.
+ * With one device the page's ReduceScatterV (tensor-parallel) and AlltoAllv
+ * (expert-parallel) exchanges are identities: the whole expert set is the one
+ * expert-parallel rank's share.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers owned by the caller (for example
+ *    allocated by PyTorch).  The library allocates nothing, keeps no state
+ *    between calls and is safe to call from several host threads.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  A
+ *    call validates its arguments on the host, enqueues its kernels on
+ *    `stream` and returns; it never synchronises.  Buffers must stay alive
+ *    and unmodified until the stream has finished the call (the page on the
+ *    DeepSeek Ascend toolchain, troubleshooting step 5: reuse or free buffers
+ *    only after the asynchronous work is done).
+ *  - Row strides are counted in elements of the row's own type.
+ *  - A failed argument check returns a non-zero moe_status and enqueues
+ *    nothing.  Problems that only the device can see (ids out of range,
+ *    repeated ids, a slot beyond the buffer) set bits of the optional
+ *    device-side `status` word and the offending pair is skipped; no write
+ *    ever leaves the caller's buffers (the DeepEP compensation PR, Kernel /
+ *    host section: fail-safe bounds guards on the scatter writes).
+ *  - No call waits on another device (same toolchain page, single-card
+ *    compute section: a local operator never holds a cross-rank wait).
+ */
+#ifndef MOE_DISPATCH_H
+#define MOE_DISPATCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,   /* a shape, range, pointer or alignment rule failed */
+    MOE_ERR_WORKSPACE = 2,     /* workspace_bytes below moe_dispatch_layout_workspace_size */
+    MOE_ERR_UNSUPPORTED = 3,   /* unknown dtype */
+    MOE_ERR_HIP = 4            /* the HIP runtime refused a launch */
+};
+
+/* Element type of the dispatched buffer. */
+enum moe_dtype {
+    MOE_BF16 = 0,              /* bfloat16 bit copy of the token row */
+    MOE_FP8_E4M3 = 1           /* OCP e4m3fn (max 448) + one fp32 scale per 128 channels */
+};
+
+/* Bits of the device-side status word. */
+enum moe_flag {
+    MOE_FLAG_ID_RANGE = 1,     /* some expert_ids value lies outside [0, num_experts) */
+    MOE_FLAG_DUP_ID = 2,       /* some row of expert_ids repeats an expert */
+    MOE_FLAG_GUARD = 4         /* some slot fell outside [0, capacity_rows): pair skipped */
+};
+
+/* Version of this interface (incremented on any signature change). */
+int moe_abi_version(void);
+
+/* Human-readable text of a moe_status value (static storage). */
+const char* moe_status_string(int status);
+
+/*
+ * Rows of the expert-contiguous buffer that always hold the padded layout,
+ * whatever the routing: with n = bs*k pairs, each expert's segment is rounded
+ * up to a multiple of `align`, so the total is at most
+ *   align * floor((n + (align-1) * min(num_experts, n)) / align).
+ * This is the padded form of the page's rule that A, the number of rows a
+ * card receives, be at least BS * min(local_expert_num, K) per source card
+ * (npu_moe_distribute_combine, constraint notes on A).  Returns -1 when the
+ * arguments break the rules of moe_dispatch_layout.
+ */
+int64_t moe_dispatch_capacity(int32_t bs, int32_t k, int32_t num_experts, int32_t align);
+
+/* Bytes of device workspace moe_dispatch_layout needs for this shape (0 when
+ * the whole layout fits one workgroup; then `workspace` may be NULL).
+ * Returns 0 for invalid arguments as well; the layout call reports those. */
+size_t moe_dispatch_layout_workspace_size(int32_t bs, int32_t k, int32_t num_experts);
+
+/*
+ * Layout: routing -> per-expert counts, padded prefix sum, stable ranks.
+ *
+ * Follows the parameters expert_ids, expand_idx and ep_send_counts of the
+ * npu_moe_distribute_combine page (which are the paired dispatch operator's
+ * outputs) and the 128-row M-tile padding of the grouped GEMM in the TEMPO
+ * summary (section 1, padded compute).
+ *
+ *  expert_ids     in  int32 [bs, k], row-major, contiguous.  Values must lie in
+ *                     [0, num_experts) and be distinct within a row (page rule).
+ *  bs             in  tokens, >= 0 (0 is an empty batch: counts and offsets 0).
+ *  k              in  experts per token, 1 <= k <= min(16, num_experts).
+ *  num_experts    in  1 <= num_experts <= 512.
+ *  align          in  segment alignment in rows, a power of two in [1, 1024];
+ *                     128 matches the grouped GEMM's M-tile.
+ *  expert_counts  out int32 [num_experts]: c_e = number of pairs routed to e.
+ *  ep_send_counts out int32 [num_experts + 1]: exclusive prefix of the padded
+ *                     counts ceil(c_e/align)*align; entry num_experts is the
+ *                     padded total M_pad.  Every entry is a multiple of align.
+ *  expand_idx     out int32 [bs * k]: for pair (t, j), the number of pairs
+ *                     (t', j') before it in row-major order routed to the same
+ *                     expert (the within-expert rank), or -1 if its id is out
+ *                     of range.  Pair (t, j) lives in row
+ *                     ep_send_counts[expert_ids[t,j]] + expand_idx[t*k+j].
+ *  status         out int32 [1] or NULL: OR of MOE_FLAG_ID_RANGE and
+ *                     MOE_FLAG_DUP_ID, overwritten (not accumulated).
+ *                     Out-of-range pairs are excluded from the counts;
+ *                     repeated ids are laid out like distinct ones.
+ *  workspace      in  device scratch of workspace_bytes >=
+ *                     moe_dispatch_layout_workspace_size(bs, k, num_experts),
+ *                     16-byte aligned; contents need no initialisation.
+ * The result is deterministic (no atomics decide any position).
+ */
+int moe_dispatch_layout(const int32_t* expert_ids, int32_t bs, int32_t k, int32_t num_experts,
+                        int32_t align, int32_t* expert_counts, int32_t* ep_send_counts,
+                        int32_t* expand_idx, int32_t* status, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Dispatch: scatter token rows into the expert-contiguous buffer.
+ *
+ * The inverse path of the combine on the npu_moe_distribute_combine page
+ * (function description: combine retraces the dispatch path); expand_x is
+ * that page's (max(tp,1)*A, H) input, here [capacity_rows, hidden].  With
+ * out_dtype MOE_FP8_E4M3 the rows are quantised on the way, the page's
+ * comm_quant_mode "quantised transfer" (its dtype is unreadable on the page;
+ * e4m3fn with per-128-channel scales is this library's reading).
+ *
+ *  x              in  bf16 [bs, hidden], row stride x_stride (>= hidden);
+ *                     base 16-byte aligned, x_stride*2 a multiple of 16.
+ *  hidden         in  > 0, a multiple of 32 (page rule on H), <= 65536;
+ *                     a multiple of 128 for MOE_FP8_E4M3.
+ *  expert_ids, expand_idx, ep_send_counts
+ *                 in  the layout call's input and outputs, unchanged.
+ *  expand_x       out [capacity_rows, hidden] of out_dtype, row stride
+ *                     expand_x_stride (>= hidden); 16-byte aligned, stride in
+ *                     bytes a multiple of 16.  Row slot(t,j) receives token t
+ *                     for every pair j.  Padding rows are NOT written.
+ *  capacity_rows  in  rows of expand_x (size it with moe_dispatch_capacity).
+ *  quant_scales   out fp32 [capacity_rows, hidden/128] row-major when
+ *                     out_dtype is MOE_FP8_E4M3 (else ignored, may be NULL):
+ *                     s = amax/448 over the 128 channels of the block;
+ *                     the code is e4m3(x/s) rounded to nearest even and
+ *                     saturated to +-448 (all-zero block: s = 0, codes 0).
+ *                     Dequantise as e4m3_value * s.
+ *  status         in/out int32 [1] or NULL: MOE_FLAG_GUARD is OR-ed in when a
+ *                     slot falls outside [0, capacity_rows); never cleared.
+ */
+int moe_dispatch(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
+                 const int32_t* expert_ids, const int32_t* expand_idx,
+                 const int32_t* ep_send_counts, int32_t k, int32_t num_experts, void* expand_x,
+                 int64_t expand_x_stride, int64_t capacity_rows, int32_t out_dtype,
+                 float* quant_scales, int32_t* status, void* stream);
+
+/*
+ * Combine: gather each token's K expert-output rows back and form
+ *   x_out[t,:] = sum_j expert_scales[t,j] * expand_x[slot(t,j), :] + shared_expert_x[t,:]
+ * (the formula of the npu_moe_distribute_combine page, with the shared expert
+ * added without a weight as its expert_scales parameter note states).
+ *
+ * Arithmetic: fp32, a fused multiply-add chain over j = 0..k-1 in order,
+ * starting from +0; then the shared row is added; then one round to nearest
+ * even into bf16.  Pairs with expand_idx < 0 or an out-of-range id contribute
+ * nothing.
+ *
+ *  expand_x       in  bf16 expert outputs [capacity_rows, hidden], row stride
+ *                     expand_x_stride; 16-byte aligned, stride*2 % 16 == 0.
+ *  expert_ids, expand_idx, ep_send_counts
+ *                 in  the same layout outputs the dispatch used.
+ *  expert_scales  in  fp32 [bs, k] row-major, contiguous.
+ *  shared_expert_x in bf16 [bs, hidden], row stride shared_stride, or NULL.
+ *  x_out          out bf16 [bs, hidden], contiguous (the page requires a
+ *                     contiguous output), 16-byte aligned.
+ *  status         in/out int32 [1] or NULL: MOE_FLAG_GUARD OR-ed in as above.
+ */
+int moe_combine(const void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
+                const int32_t* expert_ids, const int32_t* expand_idx,
+                const int32_t* ep_send_counts, const float* expert_scales,
+                const void* shared_expert_x, int64_t shared_stride, int32_t bs, int32_t hidden,
+                int32_t k, int32_t num_experts, void* x_out, int32_t* status, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DISPATCH_H */

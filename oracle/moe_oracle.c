@@ -165,13 +165,13 @@ static int is_pow2(int32_t v) { return v > 0 && (v & (v - 1)) == 0; }
  * (npu_moe_distribute_combine parameter and constraint notes); the library
  * further caps k at 16 (the widest top-K limit on that page) and requires the
  * alignment to be a power of two in [1, 1024]; bs*k and the padded total must
- * fit int32. */
+ * not exceed 2^30. */
 int oracle_check_layout_args(int32_t bs, int32_t k, int32_t num_experts, int32_t align) {
     if (bs < 0) return ORC_ERR_INVALID_ARG;
     if (num_experts < 1 || num_experts > 512) return ORC_ERR_INVALID_ARG;
     if (k < 1 || k > 16 || k > num_experts) return ORC_ERR_INVALID_ARG;
     if (!is_pow2(align) || align > 1024) return ORC_ERR_INVALID_ARG;
-    if (oracle_capacity(bs, k, num_experts, align) > 2147483647LL) return ORC_ERR_INVALID_ARG;
+    if (oracle_capacity(bs, k, num_experts, align) > (1LL << 30)) return ORC_ERR_INVALID_ARG;
     return ORC_OK;
 }
 

@@ -1,0 +1,153 @@
+"""The C-ABI library loads without a GPU, exports every function that
+include/*.h declares, and its host-side rules agree with the oracle's.
+
+Only calls that return before touching the HIP runtime are made here (size
+queries and argument checks that fail); no kernel is launched.
+"""
+
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DECL = re.compile(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\**\s+\**\s*(moe_\w+)\s*\(", re.M)
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        names |= set(DECL.findall(open(h).read()))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import combine_moe_dispatch_layout_amd as m
+    return m.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_dispatch_layout", "moe_dispatch", "moe_combine", "moe_dispatch_capacity",
+              "moe_dispatch_layout_workspace_size", "moe_status_string", "moe_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import combine_moe_dispatch_layout_amd as m
+    out = subprocess.run(["nm", "-D", "--defined-only", m.library_path()], check=True,
+                         capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.moe_abi_version() == 1
+    for code in range(5):
+        assert lib.moe_status_string(code)
+    assert b"unknown" in lib.moe_status_string(99)
+
+
+def test_capacity_matches_oracle(lib):
+    rng = np.random.default_rng(0)
+    for _ in range(2000):
+        e = int(rng.integers(-2, 520))
+        k = int(rng.integers(-1, 18))
+        bs = int(rng.integers(-2, 100000))
+        a = int(rng.choice([0, 1, 2, 3, 64, 128, 1024, 2048]))
+        ours = lib.moe_dispatch_capacity(bs, k, e, a)
+        if oracle.check_layout_args(bs, k, e, a) == oracle.OK:
+            assert ours == oracle.capacity(bs, k, e, a)
+        else:
+            assert ours == -1
+
+
+def test_workspace_size(lib):
+    assert lib.moe_dispatch_layout_workspace_size(128, 8, 256) == 0  # one workgroup
+    big = lib.moe_dispatch_layout_workspace_size(16384, 8, 512)
+    assert big >= 32 * 512 * 4  # one histogram row per workgroup
+    assert lib.moe_dispatch_layout_workspace_size(4, 9, 8) == 0  # invalid -> 0
+
+
+def _i(v):
+    return ctypes.c_void_p(v)
+
+
+FAKE = 0x1000  # a non-null, 16-byte aligned address never dereferenced
+
+
+@pytest.mark.parametrize("bs,k,e,align", [(4, 1, 0, 128), (4, 1, 513, 128), (4, 0, 8, 128),
+                                          (4, 9, 8, 128), (4, 17, 64, 128), (4, 2, 8, 3),
+                                          (-1, 2, 8, 128), (1 << 28, 16, 512, 128)])
+def test_layout_rejects_like_the_oracle(lib, bs, k, e, align):
+    assert oracle.check_layout_args(bs, k, e, align) == oracle.ERR_INVALID_ARG
+    rc = lib.moe_dispatch_layout(FAKE, bs, k, e, align, FAKE, FAKE, FAKE, None, None, 0, None)
+    assert rc == 1
+
+
+def test_layout_rejects_missing_workspace(lib):
+    rc = lib.moe_dispatch_layout(FAKE, 16384, 8, 256, 128, FAKE, FAKE, FAKE, None, None, 0, None)
+    assert rc == 2
+    rc = lib.moe_dispatch_layout(FAKE, 16384, 8, 256, 128, FAKE, FAKE, FAKE, None, FAKE + 8,
+                                 1 << 20, None)  # misaligned workspace
+    assert rc == 2
+
+
+def test_layout_rejects_null_outputs(lib):
+    assert lib.moe_dispatch_layout(FAKE, 4, 2, 8, 128, None, FAKE, FAKE, None, None, 0, None) == 1
+    assert lib.moe_dispatch_layout(None, 4, 2, 8, 128, FAKE, FAKE, FAKE, None, None, 0, None) == 1
+
+
+@pytest.mark.parametrize("hidden,dtype,code", [(0, 0, 1), (48, 0, 1), (96, 1, 1), (64, 2, 3),
+                                               (65568, 0, 1)])
+def test_dispatch_row_rules(lib, hidden, dtype, code):
+    if hidden <= 65536:
+        assert oracle.check_row_args(hidden, dtype) == code
+    rc = lib.moe_dispatch(FAKE, max(hidden, 1), 4, hidden, FAKE, FAKE, FAKE, 2, 8, FAKE,
+                          max(hidden, 1), 64, dtype, FAKE, None, None)
+    assert rc == code
+
+
+def test_dispatch_alignment_rules(lib):
+    # misaligned x base, stride not a multiple of 16 bytes, stride < hidden
+    assert lib.moe_dispatch(FAKE + 2, 64, 4, 64, FAKE, FAKE, FAKE, 2, 8, FAKE, 64, 64, 0,
+                            None, None, None) == 1
+    assert lib.moe_dispatch(FAKE, 68, 4, 64, FAKE, FAKE, FAKE, 2, 8, FAKE, 64, 64, 0,
+                            None, None, None) == 1
+    assert lib.moe_dispatch(FAKE, 32, 4, 64, FAKE, FAKE, FAKE, 2, 8, FAKE, 64, 64, 0,
+                            None, None, None) == 1
+    # fp8 without scales
+    assert lib.moe_dispatch(FAKE, 128, 4, 128, FAKE, FAKE, FAKE, 2, 8, FAKE, 128, 64, 1,
+                            None, None, None) == 1
+    # negative capacity
+    assert lib.moe_dispatch(FAKE, 64, 4, 64, FAKE, FAKE, FAKE, 2, 8, FAKE, 64, -1, 0,
+                            None, None, None) == 1
+
+
+def test_combine_rules(lib):
+    args = dict(x=FAKE, xs=64, cap=64, ids=FAKE, idx=FAKE, send=FAKE, sc=FAKE, sh=None, ss=0,
+                bs=4, h=64, k=2, e=8, out=FAKE)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.moe_combine(a["x"], a["xs"], a["cap"], a["ids"], a["idx"], a["send"], a["sc"],
+                               a["sh"], a["ss"], a["bs"], a["h"], a["k"], a["e"], a["out"],
+                               None, None)
+
+    assert call(h=48) == 1
+    assert call(sc=None) == 1
+    assert call(out=FAKE + 4) == 1
+    assert call(sh=FAKE, ss=32) == 1       # shared stride < hidden
+    assert call(sh=FAKE + 2, ss=64) == 1   # misaligned shared
+    assert call(k=9) == 1
+    assert call(cap=-5) == 1
+    assert call(bs=0) == 0                 # empty batch: nothing to launch

@@ -1,0 +1,431 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: layout, ranks and dispatched bf16 rows bit-exact; e4m3 codes and scales
+bit-exact (both sides decide each code in fp32 with a correctly rounded
+division and round-to-nearest-even); combine within 1 bf16 ulp of the oracle
+(identical fp32 FMA order, so 0 is expected and asserted as well).  Small
+cases compare every element, including the untouched padding rows; the
+full-size workloads compare the whole layout, every dispatched row (against
+the oracle's slots) and a sample of combined tokens computed by the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    import combine_moe_dispatch_layout_amd as moe
+    moe.load_library()
+    assert torch.cuda.is_available()
+    return moe
+
+
+def moe_mod():
+    import combine_moe_dispatch_layout_amd as moe
+    return moe
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def bf16_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def random_ids(rng, bs, e, k):
+    return np.argsort(rng.random((bs, e)), axis=1)[:, :k].astype(np.int32)
+
+
+def random_bf16(rng, shape):
+    return oracle.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+
+
+def gpu_layout(ids, e, align):
+    moe = moe_mod()
+    lay = moe.moe_dispatch_layout(dev(ids), e, align)
+    torch.cuda.synchronize()
+    return (lay.expert_counts.cpu().numpy(), lay.ep_send_counts.cpu().numpy(),
+            lay.expand_idx.cpu().numpy(), int(lay.status.cpu()[0]), lay)
+
+
+def assert_layout_equal(ids, e, align):
+    c, s, r, f = oracle.layout(ids, e, align)
+    gc, gs, gr, gf, lay = gpu_layout(ids, e, align)
+    np.testing.assert_array_equal(gc, c)
+    np.testing.assert_array_equal(gs, s)
+    np.testing.assert_array_equal(gr, r)
+    assert gf == f
+    return (c, s, r, f), lay
+
+
+def ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Distance in bf16 units in the last place (sign-magnitude aware)."""
+    def ordered(b):
+        b = b.astype(np.int32)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+# ------------------------------------------------------------------ layout
+
+def test_layout_random_shapes():
+    rng = np.random.default_rng(100)
+    shapes = [(1, 1, 1), (7, 3, 2), (300, 512, 16), (1000, 64, 16), (4096, 256, 8),
+              (513, 17, 16), (8192, 8, 1), (8193, 8, 1), (4097, 2, 2), (2000, 512, 5)]
+    for _ in range(30):
+        e = int(rng.integers(1, 513))
+        k = int(rng.integers(1, min(e, 16) + 1))
+        shapes.append((int(rng.integers(1, 1500)), e, k))
+    for bs, e, k in shapes:
+        for align in (1, 128):
+            assert_layout_equal(random_ids(rng, bs, e, k), e, align)
+
+
+def test_layout_edge_cases():
+    rng = np.random.default_rng(101)
+    assert_layout_equal(np.zeros((0, 4), np.int32), 16, 128)            # empty batch
+    assert_layout_equal(np.zeros((5, 1), np.int32), 1, 128)             # one expert
+    e = 16
+    assert_layout_equal(np.stack([rng.permutation(e) for _ in range(700)]).astype(np.int32),
+                        e, 128)                                         # K = E
+    hot = np.array([200, 3, 77, 5, 150, 9, 255, 0], np.int32)
+    (c, s, r, f), _ = assert_layout_equal(np.tile(hot, (20000, 1)), 256, 128)  # one hot set
+    assert c[hot].min() == 20000
+    # exactly at / just past the one-workgroup limit, and ragged tails
+    for n in (8191, 8192, 8193, 12288, 12289):
+        assert_layout_equal(random_ids(rng, n, 64, 1), 64, 128)
+
+
+def test_layout_invalid_and_repeated_ids():
+    rng = np.random.default_rng(102)
+    for bs, e, k in [(50, 8, 3), (3000, 100, 6)]:
+        ids = random_ids(rng, bs, e, k)
+        bad = rng.random(ids.shape) < 0.05
+        ids[bad] = rng.choice([-1, e, e + 7, -1000], size=bad.sum())
+        (c, s, r, f), _ = assert_layout_equal(ids, e, 128)
+        assert f & oracle.FLAG_ID_RANGE
+        ids2 = random_ids(rng, bs, e, k)
+        ids2[::7, -1] = ids2[::7, 0]
+        (c, s, r, f), _ = assert_layout_equal(ids2, e, 128)
+        assert f == oracle.FLAG_DUP_ID
+
+
+def test_layout_is_deterministic():
+    w = workloads.WORKLOADS["large"]
+    ids = workloads.routing(w.bs, w.experts, w.topk, w.routing, w.alpha, w.seed)
+    ref = None
+    moe = moe_mod()
+    d = dev(ids)
+    for _ in range(20):
+        lay = moe.moe_dispatch_layout(d, w.experts, 128)
+        cur = torch.cat([lay.expert_counts, lay.ep_send_counts, lay.expand_idx]).cpu()
+        if ref is None:
+            ref = cur
+        assert torch.equal(cur, ref)
+
+
+# ------------------------------------------------------------------ dispatch
+
+def run_dispatch_bf16(ids, x_bits, e, align, x_stride=None, out_stride=None, cap=None):
+    moe = moe_mod()
+    bs, h = x_bits.shape
+    c, s, r, _ = oracle.layout(ids, e, align)
+    cap = oracle.capacity(bs, ids.shape[1], e, align) if cap is None else cap
+    xs = h if x_stride is None else x_stride
+    os_ = h if out_stride is None else out_stride
+    x_full = np.zeros((bs, xs), np.uint16)
+    x_full[:, :h] = x_bits
+    xd = bf16_dev(x_full)[:, :h]
+    out_full = torch.full((cap, os_), 0, dtype=torch.int16, device=DEV)
+    out_full.fill_(np.int16(np.uint16(oracle.SENTINEL_BF16).view(np.int16)))
+    out = out_full.view(torch.bfloat16)[:, :h]
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    moe.moe_dispatch(xd, dev(ids), dev(r), dev(s), e, expand_x=out, capacity_rows=cap,
+                     status=status)
+    torch.cuda.synchronize()
+    ref, rflags = oracle.dispatch_bf16(x_bits, ids, r, s, e, cap)
+    got = host_bits(out_full.view(torch.bfloat16))
+    return got, ref, int(status.cpu()[0]), rflags
+
+
+@pytest.mark.parametrize("bs,h,e,k,align", [(1, 32, 1, 1, 1), (16, 128, 8, 2, 128),
+                                            (37, 1056, 40, 5, 8), (300, 4096, 256, 8, 128),
+                                            (129, 7168, 64, 16, 128), (64, 96, 3, 3, 1)])
+def test_dispatch_bf16_every_element(bs, h, e, k, align):
+    rng = np.random.default_rng(bs * 1000 + h)
+    ids = random_ids(rng, bs, e, k)
+    x = random_bf16(rng, (bs, h))
+    got, ref, gflags, rflags = run_dispatch_bf16(ids, x, e, align)
+    assert gflags == rflags == 0
+    np.testing.assert_array_equal(got[:, :h], ref)  # padding rows keep the sentinel on both
+
+
+def test_dispatch_bf16_strided_rows():
+    rng = np.random.default_rng(5)
+    ids = random_ids(rng, 100, 32, 4)
+    x = random_bf16(rng, (100, 512))
+    got, ref, _, _ = run_dispatch_bf16(ids, x, 32, 128, x_stride=512 + 64, out_stride=512 + 8)
+    np.testing.assert_array_equal(got[:, :512], ref)
+    assert np.all(got[:, 512:] == oracle.SENTINEL_BF16)  # stride gap untouched
+
+
+def test_dispatch_guard_keeps_writes_in_bounds():
+    """Capacity one row short of the padded total: the pair landing on the
+    missing row is skipped and flagged, and the canary rows after the buffer
+    are untouched."""
+    moe = moe_mod()
+    rng = np.random.default_rng(6)
+    e, k, bs, h = 4, 2, 40, 64
+    ids = random_ids(rng, bs, e, k)
+    c, s, r, _ = oracle.layout(ids, e, 1)
+    cap = int(s[-1]) - 1
+    canary = 8
+    buf = torch.full((cap + canary, h), 0x1234, dtype=torch.int16, device=DEV)
+    out = buf.view(torch.bfloat16)[:cap]
+    x = random_bf16(rng, (bs, h))
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    moe.moe_dispatch(bf16_dev(x), dev(ids), dev(r), dev(s), e, expand_x=out, capacity_rows=cap,
+                     status=status)
+    y = torch.zeros((cap, h), dtype=torch.bfloat16, device=DEV)
+    ycomb = moe.moe_combine(y, dev(ids), dev(r), dev(s),
+                            dev(np.ones((bs, k), np.float32)), None, e, status=status)
+    torch.cuda.synchronize()
+    assert int(status.cpu()[0]) == oracle.FLAG_GUARD
+    assert torch.all(buf[cap:] == 0x1234)
+    ref, rflags = oracle.dispatch_bf16(x, ids, r, s, e, cap)
+    assert rflags == oracle.FLAG_GUARD
+    got = host_bits(out)
+    written = ref != oracle.SENTINEL_BF16
+    np.testing.assert_array_equal(got[written], ref[written])
+    assert ycomb.shape == (bs, h)
+
+
+def run_dispatch_fp8(ids, x_bits, e, align):
+    moe = moe_mod()
+    bs, h = x_bits.shape
+    c, s, r, _ = oracle.layout(ids, e, align)
+    cap = oracle.capacity(bs, ids.shape[1], e, align)
+    codes = torch.full((cap, h), oracle.SENTINEL_FP8, dtype=torch.uint8, device=DEV)
+    scales = torch.full((cap, h // 128), oracle.SENTINEL_SCALE, dtype=torch.float32, device=DEV)
+    moe.moe_dispatch(bf16_dev(x_bits), dev(ids), dev(r), dev(s), e, out_dtype="fp8",
+                     expand_x=codes, quant_scales=scales, capacity_rows=cap)
+    torch.cuda.synchronize()
+    rc, rs, _ = oracle.dispatch_fp8(x_bits, ids, r, s, e, cap)
+    return codes.cpu().numpy(), scales.cpu().numpy(), rc, rs
+
+
+@pytest.mark.parametrize("bs,h,e,k", [(1, 128, 1, 1), (16, 128, 8, 2), (50, 1024, 32, 4),
+                                      (200, 7168, 256, 8), (33, 384, 16, 16)])
+def test_dispatch_fp8_every_element(bs, h, e, k):
+    rng = np.random.default_rng(bs + h)
+    ids = random_ids(rng, bs, e, k)
+    x = random_bf16(rng, (bs, h))
+    x[0, :128] = 0                 # an all-zero block
+    x[-1, -128:] = 0x8000          # a block of negative zeros
+    gc, gs, rc, rs = run_dispatch_fp8(ids, x, e, 128)
+    np.testing.assert_array_equal(gc, rc)
+    np.testing.assert_array_equal(gs.view(np.uint32), rs.view(np.uint32))
+
+
+def test_fp8_codes_for_every_bf16_value():
+    """Every finite bf16 value v with |v| <= 448 quantised in a block whose
+    amax is exactly 448 (scale 1: the code is e4m3(v), ties included) and in
+    blocks with scales that are not powers of two."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.bf16_bits_to_f32(bits)
+    keep = np.isfinite(vals) & (np.abs(vals) <= 448)
+    pool = bits[keep]
+    rows = []
+    for amax in (448.0, 300.0, 1.0, 3.0e-3):
+        amax_bits = oracle.f32_to_bf16_bits(np.array([amax], np.float32))[0]
+        av = oracle.bf16_bits_to_f32(np.array([amax_bits]))[0]
+        cand = pool[np.abs(oracle.bf16_bits_to_f32(pool)) <= av]
+        n_blocks = -(-cand.size // 127)
+        padded = np.concatenate([cand, np.zeros(n_blocks * 127 - cand.size, np.uint16)])
+        blocks = np.concatenate([np.full((n_blocks, 1), amax_bits, np.uint16),
+                                 padded.reshape(n_blocks, 127)], axis=1)
+        rows.append(blocks.reshape(-1, 1024) if blocks.size % 1024 == 0 else
+                    np.concatenate([blocks.ravel(), np.zeros((-blocks.size) % 1024,
+                                                             np.uint16)]).reshape(-1, 1024))
+    x = np.concatenate(rows)
+    bs = x.shape[0]
+    ids = np.zeros((bs, 1), np.int32)
+    gc, gs, rc, rs = run_dispatch_fp8(ids, x, 1, 1)
+    np.testing.assert_array_equal(gs.view(np.uint32), rs.view(np.uint32))
+    np.testing.assert_array_equal(gc, rc)
+
+
+# ------------------------------------------------------------------ combine
+
+def run_combine(ids, y_bits, scales, shared_bits, e, align, idx_override=None, y_stride=None):
+    moe = moe_mod()
+    c, s, r, _ = oracle.layout(ids, e, align)
+    if idx_override is not None:
+        r = idx_override
+    cap, h = y_bits.shape
+    ys = h if y_stride is None else y_stride
+    y_full = np.zeros((cap, ys), np.uint16)
+    y_full[:, :h] = y_bits
+    yd = bf16_dev(y_full)[:, :h]
+    sh = None if shared_bits is None else bf16_dev(shared_bits)
+    out = moe.moe_combine(yd, dev(ids), dev(r), dev(s), dev(scales), sh, e)
+    torch.cuda.synchronize()
+    ref, _ = oracle.combine(y_bits, ids, r, s, scales, shared_bits, e)
+    return host_bits(out), ref
+
+
+@pytest.mark.parametrize("bs,h,e,k,shared", [(1, 32, 1, 1, False), (16, 128, 8, 2, False),
+                                             (77, 1056, 40, 5, True), (300, 4096, 256, 8, True),
+                                             (65, 7168, 64, 16, True), (50, 7168, 512, 8, False)])
+def test_combine_every_element(bs, h, e, k, shared):
+    rng = np.random.default_rng(bs * 7 + k)
+    ids = random_ids(rng, bs, e, k)
+    cap = oracle.capacity(bs, k, e, 128)
+    y = random_bf16(rng, (cap, h))
+    sc = workloads.scales(bs, k, seed=bs)
+    sh = random_bf16(rng, (bs, h)) if shared else None
+    got, ref = run_combine(ids, y, sc, sh, e, 128)
+    assert ulp_diff(got, ref).max() <= 1
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_combine_strided_y_and_skipped_pairs():
+    rng = np.random.default_rng(8)
+    bs, h, e, k = 120, 512, 16, 4
+    ids = random_ids(rng, bs, e, k)
+    c, s, r, _ = oracle.layout(ids, e, 128)
+    r = r.copy()
+    r[::5] = -1                             # pairs dropped by the caller
+    cap = oracle.capacity(bs, k, e, 128)
+    y = random_bf16(rng, (cap, h))
+    sc = workloads.scales(bs, k, seed=3)
+    got, ref = run_combine(ids, y, sc, random_bf16(rng, (bs, h)), e, 128, idx_override=r,
+                           y_stride=h + 24)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_identity_round_trip_on_gpu():
+    """layout -> dispatch -> combine with y = dispatched rows, scales summing
+    to 1 and no shared row returns x bit for bit."""
+    moe = moe_mod()
+    rng = np.random.default_rng(9)
+    bs, h, e, k = 1000, 2048, 64, 8
+    ids = random_ids(rng, bs, e, k)
+    x = random_bf16(rng, (bs, h))
+    xd = bf16_dev(x)
+    lay = moe.moe_dispatch_layout(dev(ids), e, 128)
+    ex = moe.moe_dispatch(xd, dev(ids), lay.expand_idx, lay.ep_send_counts, e)
+    out = moe.moe_combine(ex, dev(ids), lay.expand_idx, lay.ep_send_counts,
+                          dev(workloads.scales(bs, k, seed=1)), None, e)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(oracle.bf16_bits_to_f32(host_bits(out)),
+                                  oracle.bf16_bits_to_f32(x))
+    assert int(lay.status.cpu()[0]) == 0
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def fp8_metrics_dev(codes, scales, x, slots, tok):
+    """Max relative error (floor 2^-6 * s) and min row / global cosine of the
+    dequantised rows against x, in float64 on the device."""
+    q = codes[slots].view(torch.float8_e4m3fn).to(torch.float64)
+    s = scales[slots].to(torch.float64).repeat_interleave(128, dim=1)
+    deq = q * s
+    xv = x[tok].to(torch.float64)
+    denom = torch.maximum(xv.abs(), s * 2.0 ** -6)
+    rel = torch.where(denom > 0, (deq - xv).abs() / torch.where(denom > 0, denom, 1), 0)
+    num = (deq * xv).sum(1)
+    den = torch.sqrt((deq * deq).sum(1) * (xv * xv).sum(1))
+    cos_rows = torch.where(den > 0, num / torch.where(den > 0, den, 1), 1)
+    cos_all = (deq * xv).sum() / torch.sqrt((deq * deq).sum() * (xv * xv).sum())
+    return float(rel.max()), float(cos_rows.min()), float(cos_all)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "skewed", "fp8", "large"])
+def test_workload_full_size(name):
+    moe = moe_mod()
+    w = workloads.WORKLOADS[name]
+    print(f"[workload {name}] bs={w.bs} H={w.hidden} E={w.experts} K={w.topk}", flush=True)
+    cap = moe.moe_dispatch_capacity(w.bs, w.topk, w.experts, w.align)
+    assert cap == oracle.capacity(w.bs, w.topk, w.experts, w.align)
+    inp = workloads.make(w, rows_y=cap)
+    ids = inp["expert_ids"]
+    sc = inp["expert_scales"]
+
+    # layout: every element
+    (c, s, r, f), lay = assert_layout_equal(ids, w.experts, w.align)
+    assert f == 0
+    ids_d = dev(ids)
+    x_d = inp["x"].to(DEV)
+    slots = torch.from_numpy(s[ids.ravel()].astype(np.int64) + r).to(DEV)
+    tok = torch.arange(w.bs, device=DEV).repeat_interleave(w.topk)
+    rng = np.random.default_rng(w.seed + 50)
+    sample = np.unique(np.concatenate([[0, w.bs - 1], rng.integers(0, w.bs, 62)]))
+
+    # dispatch
+    if w.fp8:
+        codes, qs = moe.moe_dispatch(x_d, ids_d, lay.expand_idx, lay.ep_send_counts, w.experts,
+                                     out_dtype="fp8", capacity_rows=cap)
+        torch.cuda.synchronize()
+        x_bits = workloads.bits(inp["x"])
+        s2 = slots.view(w.bs, w.topk).cpu().numpy()
+        codes_h = codes[slots.view(w.bs, w.topk)[torch.from_numpy(sample).to(DEV)]].cpu().numpy()
+        qs_h = qs[slots.view(w.bs, w.topk)[torch.from_numpy(sample).to(DEV)]].cpu().numpy()
+        for n, t in enumerate(sample):
+            q_ref, s_ref = oracle.quantize_row_e4m3(x_bits[t])
+            for j in range(w.topk):
+                np.testing.assert_array_equal(codes_h[n, j], q_ref)
+                np.testing.assert_array_equal(qs_h[n, j].view(np.uint32), s_ref.view(np.uint32))
+        # all K copies of every token identical (whole buffer)
+        sv = slots.view(w.bs, w.topk)
+        for j in range(1, w.topk):
+            assert torch.equal(codes[sv[:, j]], codes[sv[:, 0]])
+            assert torch.equal(qs[sv[:, j]], qs[sv[:, 0]])
+        rel, cmin, call = fp8_metrics_dev(codes, qs, x_d, sv[:, 0], torch.arange(w.bs,
+                                                                              device=DEV))
+        print(f"[workload {name}] fp8 max rel {rel:.6f} min row cos {cmin:.6f} "
+              f"cos {call:.6f}", flush=True)
+        assert rel <= 0.07 and cmin >= 0.999 and call >= 0.999
+        del s2
+    else:
+        ex = moe.moe_dispatch(x_d, ids_d, lay.expand_idx, lay.ep_send_counts, w.experts,
+                              capacity_rows=cap)
+        torch.cuda.synchronize()
+        # every dispatched row equals its token's row, bit for bit
+        assert torch.equal(ex[slots].view(torch.int16), x_d[tok].view(torch.int16))
+
+    # combine
+    if w.identity_experts:
+        y_d = ex
+        y_bits = oracle.dispatch_bf16(workloads.bits(inp["x"]), ids, r, s, w.experts, cap)[0]
+    else:
+        y_d = inp["y"].to(DEV)
+        y_bits = workloads.bits(inp["y"])
+    sh = inp["shared"]
+    sh_d = None if sh is None else sh.to(DEV)
+    out = moe.moe_combine(y_d, ids_d, lay.expand_idx, lay.ep_send_counts, dev(sc), sh_d,
+                          w.experts)
+    torch.cuda.synchronize()
+    got = host_bits(out[torch.from_numpy(sample).to(DEV)])
+    ref, _ = oracle.combine(y_bits, ids[sample], r.reshape(w.bs, w.topk)[sample].ravel(), s,
+                            sc[sample], None if sh is None else workloads.bits(sh)[sample],
+                            w.experts)
+    assert ulp_diff(got, ref).max() <= 1
+    np.testing.assert_array_equal(got, ref)
+    if w.identity_experts:
+        np.testing.assert_array_equal(oracle.bf16_bits_to_f32(host_bits(out)),
+                                      oracle.bf16_bits_to_f32(workloads.bits(inp["x"])))
