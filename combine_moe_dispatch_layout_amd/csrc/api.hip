@@ -9,11 +9,13 @@
 // H <= 7168) are not adopted.  The library adds: bs >= 0, align a power of two
 // in [1, 1024], bs*k and the padded capacity at most 2^30 (so 32-bit pair
 // indices keep headroom), H <= 65536 (a
-// multiple of 128 for e4m3 output), 16-byte aligned row bases and strides.
+// multiple of 128 for e4m3 output), bs*hidden/8 < 2^31, 16-byte aligned row
+// bases and strides.
 #include <stddef.h>
 #include <stdint.h>
 
 #include "moe_internal.h"
+
 
 namespace {
 
@@ -44,6 +46,9 @@ bool row_ok(const void* base, int64_t stride, int32_t hidden, int elem) {
   if (stride < hidden || ((stride * elem) & 15) != 0) return false;
   return true;
 }
+
+// Work items of the streaming kernels are indexed in 32 bits.
+bool rows_fit(int32_t bs, int32_t hidden) { return (int64_t)bs * (hidden / 8) <= INT32_MAX; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
@@ -99,7 +104,7 @@ int moe_dispatch(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
   if (!layout_args_ok(bs, k, num_experts, 1)) return MOE_ERR_INVALID_ARG;
   if (hidden <= 0 || hidden % 32 != 0 || hidden > 65536) return MOE_ERR_INVALID_ARG;
   if (out_dtype == MOE_FP8_E4M3 && hidden % 128 != 0) return MOE_ERR_INVALID_ARG;
-  if (capacity_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (capacity_rows < 0 || !rows_fit(bs, hidden)) return MOE_ERR_INVALID_ARG;
   if (bs == 0) return MOE_OK;
   if (expert_ids == nullptr || expand_idx == nullptr || ep_send_counts == nullptr)
     return MOE_ERR_INVALID_ARG;
@@ -126,7 +131,7 @@ int moe_combine(const void* expand_x, int64_t expand_x_stride, int64_t capacity_
                 int32_t k, int32_t num_experts, void* x_out, int32_t* status, void* stream) {
   if (!layout_args_ok(bs, k, num_experts, 1)) return MOE_ERR_INVALID_ARG;
   if (hidden <= 0 || hidden % 32 != 0 || hidden > 65536) return MOE_ERR_INVALID_ARG;
-  if (capacity_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (capacity_rows < 0 || !rows_fit(bs, hidden)) return MOE_ERR_INVALID_ARG;
   if (bs == 0) return MOE_OK;
   if (expert_ids == nullptr || expand_idx == nullptr || ep_send_counts == nullptr ||
       expert_scales == nullptr)

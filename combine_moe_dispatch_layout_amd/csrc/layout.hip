@@ -4,16 +4,21 @@
 // is the grouped GEMM's 128-row M-tile from the TEMPO summary, section 1).
 //
 // Ranking pass (one or more workgroups of 8 waves):
-//   The workgroup walks its pairs in rounds of 512 (one per thread) in pair
-//   order.  Within a round each wave builds, for every expert it touches, the
-//   64-bit mask of its lanes holding that expert (LDS atomic OR: the result
-//   does not depend on the order the lanes arrive in).  A lane's rank is then
-//     count of that expert in earlier rounds           (run[e])
-//   + count in lower-numbered waves of this round      (wcnt[w'][e], w' < w)
-//   + popcount(mask & lanes below me).
-//   Nothing positional is decided by an atomic race, so the layout is
-//   deterministic.  LDS is cleared sparsely: each lowest lane of a group
-//   zeroes the one mask / count word it used.
+//   Wave w of a workgroup owns a contiguous run of 64*R pairs and walks it in
+//   R sub-rounds of 64 (one pair per lane), entirely against its own LDS
+//   slice, so no workgroup barrier is needed inside the walk:
+//     - every lane ORs its bit into mask[w][e] for its expert e (LDS atomic
+//       OR: the result does not depend on the order the lanes arrive in);
+//     - a lane's local rank = wave_run[w][e] (pairs of e in this wave's
+//       earlier sub-rounds) + popcount(mask & lanes below it);
+//     - the lowest lane of each expert group advances wave_run[w][e] and
+//       clears the mask word.
+//   LDS instructions of one wave execute in issue order, so each step sees
+//   the previous one.  After one workgroup barrier a per-expert exclusive
+//   prefix over the 8 waves turns local ranks into workgroup ranks.  Nothing
+//   positional is decided by an atomic race, so the layout is deterministic.
+// Repeated ids: each thread checks one token's K ids against each other in
+//   registers.
 // Single workgroup (<= 8192 pairs): the same kernel also writes the counts and
 //   the padded exclusive scan, so small batches take one launch.
 // Several workgroups: each writes its expert histogram to the workspace; a
@@ -65,87 +70,111 @@ __device__ void write_counts_and_offsets(int c, int32_t E, int32_t align, int* w
   if (e == 0) send[E] = total;
 }
 
+// Flags an expert (an id in [0, E)) repeated within one of the tokens whose
+// first pair lies in [begin, end).
+__device__ __forceinline__ int duplicate_flags(const int32_t* __restrict__ ids, int32_t k, int32_t E, int begin,
+                               int end) {
+  int fl = 0;
+  for (int t = (begin + k - 1) / k + (int)threadIdx.x; t * k < end; t += kLayoutThreads) {
+    int v[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) v[j] = (j < k) ? ids[t * k + j] : -1 - j;
+#pragma unroll
+    for (int a = 1; a < kMaxTopK; ++a)
+#pragma unroll
+      for (int b = 0; b < a; ++b)
+        if (a < k && v[a] == v[b] && v[a] >= 0 && v[a] < E) fl = MOE_FLAG_DUP_ID;
+  }
+  return fl;
+}
+
+template <int R>
 __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     const int32_t* __restrict__ ids, int32_t n_pairs, int32_t k, int32_t E, int32_t align,
-    int32_t rounds, int32_t pairs_per_block, int32_t* __restrict__ expand_idx,
-    int32_t* __restrict__ block_hist, int32_t* __restrict__ block_flags,
-    int32_t* __restrict__ counts, int32_t* __restrict__ send, int32_t* __restrict__ status) {
+    int32_t* __restrict__ expand_idx, int32_t* __restrict__ block_hist,
+    int32_t* __restrict__ block_flags, int32_t* __restrict__ counts, int32_t* __restrict__ send,
+    int32_t* __restrict__ status) {
   __shared__ unsigned long long mask[kLayoutWaves][kMaxExperts];  // 32 KB
-  __shared__ int wcnt[kLayoutWaves][kMaxExperts];                 // 16 KB
-  __shared__ int run[kMaxExperts];
+  __shared__ int wave_run[kLayoutWaves][kMaxExperts];             // 16 KB
   __shared__ int wave_tot[kLayoutWaves];
   __shared__ int flags_lds;
 
+  constexpr int kPairs = kLayoutThreads * R;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int begin = blockIdx.x * pairs_per_block;
-  const int end = min(n_pairs, begin + pairs_per_block);
+  const int begin = blockIdx.x * kPairs;
+  const int end = min(n_pairs, begin + kPairs);
+  const int wbase = begin + wave * (kWave * R);
 
-  // Ids are prefetched one round ahead, so a round's global load latency
-  // overlaps the previous round's LDS work.
-  int e_next = 0;
-  {
-    const int i0 = begin + tid;
-    if (rounds > 0 && i0 < end) e_next = ids[i0];
+  // All id loads of this thread first.
+  int e[R];
+#pragma unroll
+  for (int s = 0; s < R; ++s) {
+    const int i = wbase + s * kWave + lane;
+    e[s] = (i < end) ? ids[i] : 0;
   }
 
   for (int j = tid; j < kLayoutWaves * kMaxExperts; j += kLayoutThreads) {
     (&mask[0][0])[j] = 0ull;
-    (&wcnt[0][0])[j] = 0;
+    (&wave_run[0][0])[j] = 0;
   }
-  for (int j = tid; j < kMaxExperts; j += kLayoutThreads) run[j] = 0;
   if (tid == 0) flags_lds = 0;
+  int fl = duplicate_flags(ids, k, E, begin, end);
   __syncthreads();
 
-  int fl = 0;
-  for (int r = 0; r < rounds; ++r) {  // rounds is workgroup-uniform
-    const int i = begin + r * kLayoutThreads + tid;
+  const unsigned long long below_me = (1ull << lane) - 1ull;
+  int lr[R];
+#pragma unroll
+  for (int s = 0; s < R; ++s) {
+    const int i = wbase + s * kWave + lane;
     const bool in = i < end;
-    const int e = e_next;
-    {
-      const int in_next = i + kLayoutThreads;
-      e_next = (r + 1 < rounds && in_next < end) ? ids[in_next] : 0;
-    }
-    const bool ok = in && e >= 0 && e < E;
+    const bool ok = in && e[s] >= 0 && e[s] < E;
     if (in && !ok) fl |= MOE_FLAG_ID_RANGE;
-    if (ok) {
-      for (int j = i - (i % k); j < i; ++j)
-        if (ids[j] == e) fl |= MOE_FLAG_DUP_ID;
-      atomicOr(&mask[wave][e], 1ull << lane);
-    }
-    __syncthreads();
+    if (ok) atomicOr(&mask[wave][e[s]], 1ull << lane);
+    __builtin_amdgcn_wave_barrier();
     unsigned long long m = 0;
-    int lr = 0;
+    int before = 0;
     if (ok) {
-      m = mask[wave][e];
-      lr = __popcll(m & ((1ull << lane) - 1ull));
-      if (lr == 0) wcnt[wave][e] = __popcll(m);
+      m = mask[wave][e[s]];
+      before = wave_run[wave][e[s]];
     }
-    __syncthreads();
-    int rank = -1;
-    if (ok) {
-      rank = run[e] + lr;
-      for (int w = 0; w < wave; ++w) rank += wcnt[w][e];
+    __builtin_amdgcn_wave_barrier();
+    const int below = __popcll(m & below_me);
+    lr[s] = ok ? before + below : -1;
+    if (ok && below == 0) {
+      wave_run[wave][e[s]] = before + __popcll(m);
+      mask[wave][e[s]] = 0ull;
     }
-    __syncthreads();
-    if (ok && lr == 0) {
-      atomicAdd(&run[e], __popcll(m));
-      mask[wave][e] = 0ull;
-      wcnt[wave][e] = 0;
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+
+  // Exclusive prefix over waves, per expert; tot = this workgroup's count.
+  int tot = 0;
+  if (tid < E) {
+#pragma unroll
+    for (int w = 0; w < kLayoutWaves; ++w) {
+      const int c = wave_run[w][tid];
+      wave_run[w][tid] = tot;
+      tot += c;
     }
-    if (in) expand_idx[i] = rank;
   }
   if (fl) atomicOr(&flags_lds, fl);
   __syncthreads();
 
+#pragma unroll
+  for (int s = 0; s < R; ++s) {
+    const int i = wbase + s * kWave + lane;
+    if (i < end) expand_idx[i] = lr[s] >= 0 ? lr[s] + wave_run[wave][e[s]] : -1;
+  }
+
   if (block_hist == nullptr) {
     // The whole batch was this workgroup: finish the layout here.
-    const int c = (tid < E) ? run[tid] : 0;
-    write_counts_and_offsets(c, E, align, wave_tot, counts, send);
+    write_counts_and_offsets(tot, E, align, wave_tot, counts, send);
     if (tid == 0 && status) *status = flags_lds;
   } else {
-    for (int e = tid; e < E; e += kLayoutThreads) block_hist[blockIdx.x * E + e] = run[e];
+    if (tid < E) block_hist[blockIdx.x * E + tid] = tot;
     if (tid == 0) block_flags[blockIdx.x] = flags_lds;
   }
 }
@@ -161,28 +190,43 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
   const int tid = threadIdx.x;
   const bool last = (b == nblocks - 1);
 
+  __shared__ int flags_lds;
+  if (tid == 0) flags_lds = 0;
+  // Column sums over the earlier workgroups' histograms; the loads of one
+  // batch of rows are independent, so they are issued together.
   int own = 0;
   if (tid < E) {
     int s = 0;
+#pragma unroll 8
     for (int bb = 0; bb < b; ++bb) s += block_hist[bb * E + tid];
     base[tid] = s;
     if (last) own = s + block_hist[b * E + tid];
   }
   if (last) {  // workgroup-uniform
     write_counts_and_offsets(own, E, align, wave_tot, counts, send);
-    if (tid == 0 && status) {
-      int f = 0;
-      for (int bb = 0; bb < nblocks; ++bb) f |= block_flags[bb];
-      *status = f;
-    }
+    int f = 0;
+    for (int bb = tid; bb < nblocks; bb += kLayoutThreads) f |= block_flags[bb];
+    if (f) atomicOr(&flags_lds, f);
+    __syncthreads();
+    if (tid == 0 && status) *status = flags_lds;
   }
   __syncthreads();
 
+  // Every workgroup of this pass covers kLayoutMultiRounds * kLayoutThreads
+  // pairs; all of a thread's loads are issued before any of its stores.
   const int begin = b * pairs_per_block;
   const int end = min(n_pairs, begin + pairs_per_block);
-  for (int i = begin + tid; i < end; i += kLayoutThreads) {
-    const int r = expand_idx[i];
-    if (r >= 0) expand_idx[i] = r + base[ids[i]];
+  int r[kLayoutMultiRounds], e[kLayoutMultiRounds];
+#pragma unroll
+  for (int s = 0; s < kLayoutMultiRounds; ++s) {
+    const int i = begin + s * kLayoutThreads + tid;
+    r[s] = (i < end) ? expand_idx[i] : -1;
+    e[s] = (i < end) ? ids[i] : 0;
+  }
+#pragma unroll
+  for (int s = 0; s < kLayoutMultiRounds; ++s) {
+    const int i = begin + s * kLayoutThreads + tid;
+    if (r[s] >= 0) expand_idx[i] = r[s] + base[e[s]];
   }
 }
 
@@ -193,7 +237,9 @@ LayoutPlan plan_layout(int32_t bs, int32_t k) {
   p.n_pairs = (int64_t)bs * k;
   if (p.n_pairs <= (int64_t)kLayoutThreads * kLayoutSingleMaxRounds) {
     p.blocks = 1;
-    p.rounds = (int32_t)((p.n_pairs + kLayoutThreads - 1) / kLayoutThreads);
+    int r = 1;
+    while ((int64_t)r * kLayoutThreads < p.n_pairs) r *= 2;
+    p.rounds = r;
   } else {
     p.rounds = kLayoutMultiRounds;
     const int64_t ppb = (int64_t)kLayoutMultiRounds * kLayoutThreads;
@@ -210,30 +256,47 @@ size_t layout_workspace_bytes(const LayoutPlan& p, int32_t num_experts) {
   return hist_aligned + (size_t)p.blocks * sizeof(int32_t);
 }
 
+namespace {
+
+template <int R>
+void launch_rank(const LayoutPlan& plan, const int32_t* ids, int32_t k, int32_t E, int32_t align,
+                 int32_t* expand_idx, int32_t* hist, int32_t* bflags, int32_t* counts,
+                 int32_t* send, int32_t* status, hipStream_t stream) {
+  layout_rank_kernel<R><<<plan.blocks, kLayoutThreads, 0, stream>>>(
+      ids, (int32_t)plan.n_pairs, k, E, align, expand_idx, hist, bflags, counts, send, status);
+}
+
+}  // namespace
+
 hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int32_t align,
                          const LayoutPlan& plan, int32_t* counts, int32_t* send,
                          int32_t* expand_idx, int32_t* status, void* workspace,
                          hipStream_t stream) {
-  const int32_t n = (int32_t)plan.n_pairs;
-  const int32_t ppb = (int32_t)plan.pairs_per_block;
-  if (plan.blocks <= 1) {
-    layout_rank_kernel<<<1, kLayoutThreads, 0, stream>>>(ids, n, k, num_experts, align,
-                                                         plan.rounds, ppb, expand_idx, nullptr,
-                                                         nullptr, counts, send, status);
-    return hipGetLastError();
+  int32_t* hist = nullptr;
+  int32_t* bflags = nullptr;
+  if (plan.blocks > 1) {
+    hist = static_cast<int32_t*>(workspace);
+    const size_t hist_bytes = ((size_t)plan.blocks * num_experts * sizeof(int32_t) + 255) &
+                              ~(size_t)255;
+    bflags = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + hist_bytes);
   }
-  int32_t* hist = static_cast<int32_t*>(workspace);
-  const size_t hist_bytes = ((size_t)plan.blocks * num_experts * sizeof(int32_t) + 255) &
-                            ~(size_t)255;
-  int32_t* bflags = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + hist_bytes);
-  layout_rank_kernel<<<plan.blocks, kLayoutThreads, 0, stream>>>(
-      ids, n, k, num_experts, align, plan.rounds, ppb, expand_idx, hist, bflags, counts, send,
-      status);
+  switch (plan.rounds) {
+    case 1: launch_rank<1>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
+                           send, status, stream); break;
+    case 2: launch_rank<2>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
+                           send, status, stream); break;
+    case 4: launch_rank<4>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
+                           send, status, stream); break;
+    case 8: launch_rank<8>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
+                           send, status, stream); break;
+    default: launch_rank<16>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
+                             send, status, stream); break;
+  }
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || plan.blocks <= 1) return err;
   layout_finalize_kernel<<<plan.blocks, kLayoutThreads, 0, stream>>>(
-      ids, n, num_experts, align, ppb, plan.blocks, hist, bflags, expand_idx, counts, send,
-      status);
+      ids, (int32_t)plan.n_pairs, num_experts, align, (int32_t)plan.pairs_per_block, plan.blocks,
+      hist, bflags, expand_idx, counts, send, status);
   return hipGetLastError();
 }
 

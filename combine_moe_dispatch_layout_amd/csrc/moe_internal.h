@@ -30,35 +30,86 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Routes of token t: destination row slot[j] (-1 = pair skipped) and weight
-// w[j] for j < KMAX.  Lanes 0..k-1 of every wave fetch one pair each (ids,
-// expand_idx and scales in one round trip, send[e] in a second), then the
-// values are broadcast to scalar registers, so the rest of the kernel
-// branches on them uniformly.  A slot outside [0, cap) is reported through
-// `status` when `report` is set (one lane group per token does it).
-template <int KMAX>
-__device__ __forceinline__ void load_token_routes(int32_t t, const int32_t* __restrict__ ids,
-                                                  const int32_t* __restrict__ idx,
-                                                  const int32_t* __restrict__ send,
-                                                  const float* __restrict__ scales, int32_t k,
-                                                  int32_t E, int64_t cap, int64_t (&slot)[KMAX],
-                                                  float (&w)[KMAX], int32_t* status,
-                                                  bool report) {
+// Launch shapes and cache hints of the streaming kernels, chosen by
+// measurement on MI355X; each can be overridden at build time.
+#ifndef MOE_DISPATCH_THREADS
+#define MOE_DISPATCH_THREADS 128   // threads per dispatch workgroup
+#endif
+#ifndef MOE_DISPATCH_VPT
+#define MOE_DISPATCH_VPT 1         // 16-byte vectors per thread per row chunk
+#endif
+#ifndef MOE_COMBINE_THREADS
+#define MOE_COMBINE_THREADS 128
+#endif
+#ifndef MOE_COMBINE_VPT
+#define MOE_COMBINE_VPT 1
+#endif
+#ifndef MOE_FP8_THREADS
+#define MOE_FP8_THREADS 64
+#endif
+#ifndef MOE_NT_STORES
+#define MOE_NT_STORES 1            // write-once outputs bypass cache retention
+#endif
+#ifndef MOE_NT_LOADS
+#define MOE_NT_LOADS 1             // read-once expert rows bypass cache retention
+#endif
+
+template <typename T>
+__device__ __forceinline__ void store_stream(T v, T* p) {
+#if MOE_NT_STORES
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
+template <typename T>
+__device__ __forceinline__ T load_stream(const T* p) {
+#if MOE_NT_LOADS
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+// Per-token routing metadata, fetched lane-parallel: lane j < k holds pair
+// (t, j)'s expert id, within-expert rank and weight.  Loads are only issued
+// here; the values are consumed by resolve_routes.
+struct PairMeta {
+  int e = -1;
+  int r = -1;
+  float w = 0.0f;
+};
+
+__device__ __forceinline__ void fetch_pair_meta(PairMeta& m, int32_t t, int32_t k,
+                                                const int32_t* __restrict__ ids,
+                                                const int32_t* __restrict__ idx,
+                                                const float* __restrict__ scales) {
   const int lane = threadIdx.x & (kWave - 1);
-  int64_t my_slot = -1;
-  float my_w = 0.0f;
   if (lane < k) {
     const int64_t p = (int64_t)t * k + lane;
-    const int e = ids[p];
-    const int r = idx[p];
-    if (scales) my_w = scales[p];
-    if (e >= 0 && e < E && r >= 0) {
-      const int64_t s = (int64_t)send[e] + r;
-      if (s >= 0 && s < cap)
-        my_slot = s;
-      else if (report && status)
-        atomicOr(status, (int)MOE_FLAG_GUARD);
-    }
+    m.e = ids[p];
+    m.r = idx[p];
+    if (scales) m.w = scales[p];
+  }
+}
+
+// Turns fetched metadata into workgroup-uniform routes: destination row
+// slot[j] (-1 = pair skipped) and weight w[j], using the send counts staged
+// in LDS.  A slot outside [0, cap) is skipped and, when `report` is set,
+// flagged through `status`.
+template <int KMAX>
+__device__ __forceinline__ void resolve_routes(const PairMeta& m, const int* send_lds, int32_t k,
+                                               int32_t E, int64_t cap, int64_t (&slot)[KMAX],
+                                               float (&w)[KMAX], int32_t* status, bool report) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t my_slot = -1;
+  if (lane < k && m.e >= 0 && m.e < E && m.r >= 0) {
+    const int64_t s = (int64_t)send_lds[m.e] + m.r;
+    if (s >= 0 && s < cap)
+      my_slot = s;
+    else if (report && status)
+      atomicOr(status, (int)MOE_FLAG_GUARD);
   }
   const int32_t lo = (int32_t)(my_slot & 0xFFFFFFFF);
   const int32_t hi = (int32_t)(my_slot >> 32);
@@ -67,8 +118,15 @@ __device__ __forceinline__ void load_token_routes(int32_t t, const int32_t* __re
     const uint32_t l = (uint32_t)__builtin_amdgcn_readlane(lo, j);
     const int32_t h = __builtin_amdgcn_readlane(hi, j);
     slot[j] = (j < k) ? (int64_t)(((uint64_t)(uint32_t)h << 32) | l) : -1;
-    w[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
+    w[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m.w), j));
   }
+}
+
+// Copies ep_send_counts[0..E] into LDS (one pass per workgroup).
+__device__ __forceinline__ void stage_send(int* send_lds, const int32_t* __restrict__ send,
+                                           int32_t E) {
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) send_lds[e] = send[e];
+  __syncthreads();
 }
 
 // ---- layout ---------------------------------------------------------------

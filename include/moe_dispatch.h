@@ -138,7 +138,7 @@ int moe_dispatch_layout(const int32_t* expert_ids, int32_t bs, int32_t k, int32_
  *  x              in  bf16 [bs, hidden], row stride x_stride (>= hidden);
  *                     base 16-byte aligned, x_stride*2 a multiple of 16.
  *  hidden         in  > 0, a multiple of 32 (page rule on H), <= 65536;
- *                     a multiple of 128 for MOE_FP8_E4M3.
+ *                     a multiple of 128 for MOE_FP8_E4M3; bs*hidden/8 < 2^31.
  *  expert_ids, expand_idx, ep_send_counts
  *                 in  the layout call's input and outputs, unchanged.
  *  expand_x       out [capacity_rows, hidden] of out_dtype, row stride
@@ -178,6 +178,7 @@ int moe_dispatch(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
  *                 in  the same layout outputs the dispatch used.
  *  expert_scales  in  fp32 [bs, k] row-major, contiguous.
  *  shared_expert_x in bf16 [bs, hidden], row stride shared_stride, or NULL.
+ *  bs, hidden     in  as for moe_dispatch (bs*hidden/8 < 2^31).
  *  x_out          out bf16 [bs, hidden], contiguous (the page requires a
  *                     contiguous output), 16-byte aligned.
  *  status         in/out int32 [1] or NULL: MOE_FLAG_GUARD OR-ed in as above.

@@ -182,3 +182,12 @@ def test_capacity_is_tight():
         ids = np.argsort(rng.random((bs, num_experts)), axis=1)[:, :kk].astype(np.int32)
         _, s, _, _ = oracle.layout(ids.reshape(bs, kk), num_experts, a)
         assert s[-1] <= oracle.capacity(bs, kk, num_experts, a)
+
+
+def test_equal_out_of_range_ids_are_not_a_repeated_expert():
+    # "repeats" concerns experts, i.e. ids in [0, E); two equal invalid ids in
+    # a row only raise the range flag
+    ids = np.array([[-1, -1], [7, 7], [0, 1]], dtype=np.int32)
+    c, send, r, flags = oracle.layout(ids, 4, 1)
+    assert flags == oracle.FLAG_ID_RANGE
+    np.testing.assert_array_equal(r, [-1, -1, -1, -1, 0, 0])
