@@ -255,6 +255,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
                      "algorithmic_bytes_per_launch": nbytes["combine"]},
     }
     if args.cpu_seconds > 0:
