@@ -153,14 +153,13 @@ def main():
 
     moe.load_library()
     w = workloads.WORKLOADS[args.workload]
-    if w.fp8:
-        raise SystemExit("the bench line times the bf16 path; use the parity tests for fp8")
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     cap = moe.moe_dispatch_capacity(w.bs, w.topk, w.experts, w.align)
     inp = workloads.make(w, rows_y=None if w.identity_experts else cap)
 
-    nbytes = algorithmic_bytes(w.bs, w.hidden, w.experts, w.topk, inp["shared"] is not None)
+    nbytes = algorithmic_bytes(w.bs, w.hidden, w.experts, w.topk, inp["shared"] is not None,
+                               fp8=w.fp8)
     step_bytes = sum(nbytes.values())
     sets = args.sets or max(1, min(64, -(-(2 << 30) // step_bytes)))
 
@@ -171,10 +170,13 @@ def main():
     sh0 = None if inp["shared"] is None else inp["shared"].to(dev)
     bufs = []
     for i in range(sets):
-        ex = torch.empty((cap, w.hidden), dtype=torch.bfloat16, device=dev)
+        ex = torch.empty((cap, w.hidden), dtype=torch.uint8 if w.fp8 else torch.bfloat16,
+                         device=dev)
         bufs.append({
             "x": x0 if i == 0 else x0.clone(),
             "y": ex if y0 is None else (y0 if i == 0 else y0.clone()),
+            "scales": (torch.empty((cap, w.hidden // 128), dtype=torch.float32, device=dev)
+                       if w.fp8 else None),
             "shared": None if sh0 is None else (sh0 if i == 0 else sh0.clone()),
             "expand_x": ex,
             "out": torch.empty((w.bs, w.hidden), dtype=torch.bfloat16, device=dev),
@@ -188,36 +190,50 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(b, ev=None):
+        lay = moe.moe_dispatch_layout(ids, w.experts, w.align, out=b["layout"], workspace=ws)
+        moe.moe_dispatch(b["x"], ids, lay.expand_idx, lay.ep_send_counts, w.experts,
+                         expand_x=b["expand_x"], capacity_rows=cap,
+                         out_dtype="fp8" if w.fp8 else "bf16", quant_scales=b["scales"])
         if ev is not None:
             ev[0].record(stream)
-        lay = moe.moe_dispatch_layout(ids, w.experts, w.align, out=b["layout"], workspace=ws)
-        if ev is not None:
-            ev[1].record(stream)
-        moe.moe_dispatch(b["x"], ids, lay.expand_idx, lay.ep_send_counts, w.experts,
-                         expand_x=b["expand_x"], capacity_rows=cap)
-        if ev is not None:
-            ev[2].record(stream)
         moe.moe_combine(b["y"], ids, lay.expand_idx, lay.ep_send_counts, scales, b["shared"],
                         w.experts, out=b["out"])
         if ev is not None:
-            ev[3].record(stream)
+            ev[1].record(stream)
 
     for i in range(args.warmup):
         step(bufs[i % sets])
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Timed region: K steps; HIP events (2 per step, on the launch stream)
+    # bracket each combine launch for the roofline, the host clock the whole.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(bufs[i % sets], events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    com_ms = [e[0].elapsed_time(e[1]) for e in events]
 
-    lay_ms = [e[0].elapsed_time(e[1]) for e in events]
-    dis_ms = [e[1].elapsed_time(e[2]) for e in events]
-    com_ms = [e[2].elapsed_time(e[3]) for e in events]
-    gpu_ms = [e[0].elapsed_time(e[3]) for e in events]
+    # Per-kernel breakdown (outside the timed region: event records between
+    # kernels cost a few microseconds each on this runtime).
+    brk = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(10)]
+    for i, e in enumerate(brk):
+        b = bufs[i % sets]
+        e[0].record(stream)
+        lay = moe.moe_dispatch_layout(ids, w.experts, w.align, out=b["layout"], workspace=ws)
+        e[1].record(stream)
+        moe.moe_dispatch(b["x"], ids, lay.expand_idx, lay.ep_send_counts, w.experts,
+                         expand_x=b["expand_x"], capacity_rows=cap,
+                         out_dtype="fp8" if w.fp8 else "bf16", quant_scales=b["scales"])
+        e[2].record(stream)
+        moe.moe_combine(b["y"], ids, lay.expand_idx, lay.ep_send_counts, scales, b["shared"],
+                        w.experts, out=b["out"])
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    lay_ms = [e[0].elapsed_time(e[1]) for e in brk]
+    dis_ms = [e[1].elapsed_time(e[2]) for e in brk]
     mean = lambda v: sum(v) / len(v)
     ms_per_step = elapsed * 1e3 / args.steps
     status = int(bufs[0]["layout"].status.cpu()[0])
@@ -239,7 +255,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 (dispatch e4m3, fp32 scales)" if w.fp8 else "bf16",
         "data": "synthetic (seeded generators; no routing trace or trained weights)",
         "config": {"workload": w.name, "bs": w.bs, "hidden": w.hidden, "experts": w.experts,
                    "topk": w.topk, "routing": w.routing + (f"(alpha={w.alpha})"
@@ -247,7 +263,7 @@ def main():
                    "align": w.align, "capacity_rows": cap, "buffer_sets": sets,
                    "bytes_per_step": step_bytes},
         "kernels_ms": {"layout": round(mean(lay_ms), 4), "dispatch": round(mean(dis_ms), 4),
-                       "combine": round(mean(com_ms), 4), "step_gpu": round(mean(gpu_ms), 4)},
+                       "combine": round(mean(com_ms), 4)},
         "kernels_gbs": {"layout": round(nbytes["layout"] / mean(lay_ms) / 1e6, 1),
                         "dispatch": round(nbytes["dispatch"] / mean(dis_ms) / 1e6, 1),
                         "combine": round(achieved, 1)},

@@ -19,7 +19,7 @@
 //   positional is decided by an atomic race, so the layout is deterministic.
 // Repeated ids: each thread checks one token's K ids against each other in
 //   registers.
-// Single workgroup (<= 8192 pairs): the same kernel also writes the counts and
+// Single workgroup (<= 2048 pairs): the same kernel also writes the counts and
 //   the padded exclusive scan, so small batches take one launch.
 // Several workgroups: each writes its expert histogram to the workspace; a
 //   second launch gives every workgroup the column sum of the histograms of

@@ -45,7 +45,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 #define MOE_COMBINE_VPT 1
 #endif
 #ifndef MOE_FP8_THREADS
-#define MOE_FP8_THREADS 64
+#define MOE_FP8_THREADS 256
 #endif
 #ifndef MOE_NT_STORES
 #define MOE_NT_STORES 1            // write-once outputs bypass cache retention
@@ -139,8 +139,16 @@ struct LayoutPlan {
 };
 constexpr int kLayoutWaves = 8;
 constexpr int kLayoutThreads = kLayoutWaves * kWave;   // 512 pairs per round
-constexpr int kLayoutSingleMaxRounds = 16;             // one workgroup up to 8192 pairs
-constexpr int kLayoutMultiRounds = 8;                  // 4096 pairs per workgroup otherwise
+#ifndef MOE_LAYOUT_SINGLE_ROUNDS
+#define MOE_LAYOUT_SINGLE_ROUNDS 4
+#endif
+#ifndef MOE_LAYOUT_MULTI_ROUNDS
+#define MOE_LAYOUT_MULTI_ROUNDS 4
+#endif
+// One workgroup ranks up to kLayoutThreads * kLayoutSingleMaxRounds pairs by
+// itself; larger batches use workgroups of kLayoutMultiRounds rounds each.
+constexpr int kLayoutSingleMaxRounds = MOE_LAYOUT_SINGLE_ROUNDS;
+constexpr int kLayoutMultiRounds = MOE_LAYOUT_MULTI_ROUNDS;
 
 LayoutPlan plan_layout(int32_t bs, int32_t k);
 size_t layout_workspace_bytes(const LayoutPlan& p, int32_t num_experts);

@@ -105,8 +105,9 @@ def test_layout_edge_cases():
     hot = np.array([200, 3, 77, 5, 150, 9, 255, 0], np.int32)
     (c, s, r, f), _ = assert_layout_equal(np.tile(hot, (20000, 1)), 256, 128)  # one hot set
     assert c[hot].min() == 20000
-    # exactly at / just past the one-workgroup limit, and ragged tails
-    for n in (8191, 8192, 8193, 12288, 12289):
+    # at / around the one-workgroup limit (2048 pairs), the per-workgroup
+    # tile of the multi-workgroup path (2048 pairs), and ragged tails
+    for n in (511, 512, 513, 2047, 2048, 2049, 4095, 4096, 4097, 8193, 12289):
         assert_layout_equal(random_ids(rng, n, 64, 1), 64, 128)
 
 
