@@ -18,6 +18,8 @@ expert_scales / shared_expert_x; TEMPO summary section 1 for the 128-row tile):
   ``ep_send_counts[e] + expand_idx``.
 * ``combine``     -- fp32 fused-multiply-add chain over k ascending, plus the
   unweighted shared row, rounded to bf16 (nearest-even).
+* ``combine_fp8`` -- the same sum over e4m3 expert rows, each term dequantised
+  as ``e4m3_value * scale`` (one binary32 multiply) first.
 
 Parity status: every function is pinned by the ``not gpu`` tests (brute force,
 closed forms, invariants, library codecs); none is "parity unpinned".
@@ -92,6 +94,8 @@ def _load():
                                                P, P, P, P]),
         "oracle_combine": (ctypes.c_int, [P, i64, i64, P, P, P, P, P, i64, i32, i32, i32, i32,
                                           P, P]),
+        "oracle_combine_fp8": (ctypes.c_int, [P, i64, i64, P, P, P, P, P, P, i64, i32, i32,
+                                              i32, i32, P, P]),
         "oracle_f32_to_bf16_array": (None, [P, i64, P]),
         "oracle_f32_to_e4m3_array": (None, [P, i64, P]),
         "oracle_e4m3_to_f32_array": (None, [P, i64, P]),
@@ -251,6 +255,30 @@ def combine(y_bits: np.ndarray, expert_ids: np.ndarray, expand_idx: np.ndarray,
     rc = _load().oracle_combine(_ptr(y_bits), hidden, cap, _ptr(ids), _ptr(_i32(expand_idx)),
                                 _ptr(_i32(ep_send_counts)), _ptr(scales), _ptr(shared_bits),
                                 hidden, bs, hidden, k, num_experts, _ptr(out), _ptr(flags))
+    if rc != OK:
+        raise OracleArgError(rc)
+    return out, int(flags[0])
+
+
+def combine_fp8(y_codes: np.ndarray, y_scales: np.ndarray, expert_ids: np.ndarray,
+                expand_idx: np.ndarray, ep_send_counts: np.ndarray, expert_scales: np.ndarray,
+                shared_bits: np.ndarray | None, num_experts: int):
+    """``y_codes``: uint8 [capacity_rows, H] e4m3 codes; ``y_scales``: f32
+    [capacity_rows, H/128].  Returns ``(x_out uint16 [BS, H], flags)``."""
+    y_codes = np.ascontiguousarray(y_codes, dtype=np.uint8)
+    y_scales = np.ascontiguousarray(y_scales, dtype=np.float32)
+    ids = _i32(expert_ids)
+    bs, k = ids.shape
+    cap, hidden = y_codes.shape
+    scales = np.ascontiguousarray(expert_scales, dtype=np.float32)
+    if shared_bits is not None:
+        shared_bits = np.ascontiguousarray(shared_bits, dtype=np.uint16)
+    out = np.empty((bs, hidden), dtype=np.uint16)
+    flags = np.zeros(1, dtype=np.int32)
+    rc = _load().oracle_combine_fp8(_ptr(y_codes), hidden, cap, _ptr(y_scales), _ptr(ids),
+                                    _ptr(_i32(expand_idx)), _ptr(_i32(ep_send_counts)),
+                                    _ptr(scales), _ptr(shared_bits), hidden, bs, hidden, k,
+                                    num_experts, _ptr(out), _ptr(flags))
     if rc != OK:
         raise OracleArgError(rc)
     return out, int(flags[0])

@@ -28,6 +28,8 @@
  *  - FP8 dispatch: the page's comm_quant_mode parameter names a quantised
  *    transfer but its dtype is unreadable; the reading adopted is OCP e4m3fn
  *    with one fp32 scale amax/448 per (token, 128-channel block).
+ *  - FP8 combine: the same quantised transfer on the return path; expert
+ *    output rows in that e4m3 + scale format are dequantised term by term.
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *  - expand_idx[t*K+k] is the number of earlier pairs (t',k') < (t,k), in
@@ -363,6 +365,47 @@ int oracle_combine(const uint16_t* y, int64_t y_stride, int64_t capacity_rows,
                 float w = expert_scales[(int64_t)t * k + j];
                 float v = oracle_bf16_to_f32(y[slots[j] * y_stride + h]);
                 acc = fmaf(w, v, acc);
+            }
+            if (shared) acc = acc + oracle_bf16_to_f32(shared[(int64_t)t * shared_stride + h]);
+            x_out[(int64_t)t * hidden + h] = oracle_f32_to_bf16(acc);
+        }
+    }
+    if (flags) *flags |= f;
+    return ORC_OK;
+}
+
+/* Quantised-transfer combine (the combine page's comm_quant_mode on the return
+ * path; the dtype is unreadable there, read as the same e4m3 + per-128-channel
+ * fp32 scale format the dispatch emits): expert output rows arrive as codes
+ * y[slot, :] with scales y_scales[slot, h/128] ([capacity_rows, hidden/128]
+ * row-major).  Each term is dequantised with one binary32 multiply,
+ *   deq = e4m3_to_f32(code) * scale,
+ * then summed exactly like the bf16 combine: fma chain over k ascending from
+ * +0, + shared, round to nearest even into bf16. */
+int oracle_combine_fp8(const uint8_t* y, int64_t y_stride, int64_t capacity_rows,
+                       const float* y_scales, const int32_t* expert_ids,
+                       const int32_t* expand_idx, const int32_t* ep_send_counts,
+                       const float* expert_scales, const uint16_t* shared,
+                       int64_t shared_stride, int32_t bs, int32_t hidden, int32_t k,
+                       int32_t num_experts, uint16_t* x_out, int32_t* flags) {
+    int rc = oracle_check_layout_args(bs, k, num_experts, 1);
+    if (rc == ORC_OK) rc = oracle_check_row_args(hidden, ORC_DTYPE_FP8_E4M3);
+    if (rc != ORC_OK) return rc;
+    int32_t f = 0;
+    int32_t nb = hidden / 128;
+    int64_t slots[16];
+    for (int32_t t = 0; t < bs; ++t) {
+        for (int32_t j = 0; j < k; ++j)
+            slots[j] = pair_slot(expert_ids, expand_idx, ep_send_counts, k, num_experts,
+                                 capacity_rows, t, j, &f);
+        for (int32_t h = 0; h < hidden; ++h) {
+            float acc = 0.0f;
+            for (int32_t j = 0; j < k; ++j) {
+                if (slots[j] < 0) continue;
+                float w = expert_scales[(int64_t)t * k + j];
+                float code = oracle_e4m3_to_f32(y[slots[j] * y_stride + h]);
+                float deq = code * y_scales[slots[j] * nb + h / 128];
+                acc = fmaf(w, deq, acc);
             }
             if (shared) acc = acc + oracle_bf16_to_f32(shared[(int64_t)t * shared_stride + h]);
             x_out[(int64_t)t * hidden + h] = oracle_f32_to_bf16(acc);
