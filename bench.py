@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="skewed",
                    choices=["tiny", "decode", "skewed", "fp8", "large"])
+    p.add_argument("--combine", default="bf16", choices=["bf16", "fp8"],
+                   help="expert-output format read by the combine (fp8 = e4m3 + scales)")
     p.add_argument("--sets", type=int, default=0,
                    help="buffer sets rotated across steps (0 = enough to exceed 2 GiB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -55,15 +57,15 @@ def parse():
 
 # ---------------------------------------------------------------- byte model
 
-def algorithmic_bytes(bs, h, e, k, shared=True, fp8=False):
+def algorithmic_bytes(bs, h, e, k, shared=True, fp8=False, fp8_combine=False):
     """Bytes each kernel must move: real rows only, metadata once per kernel."""
     layout = 4 * bs * k + 4 * bs * k + 4 * e + 4 * (e + 1)
     if fp8:
         dispatch = 2 * bs * h + bs * k * (h + 4 * (h // 128)) + 8 * bs * k + 4 * (e + 1)
     else:
         dispatch = 2 * bs * h + 2 * bs * k * h + 8 * bs * k + 4 * (e + 1)
-    combine = (2 * bs * k * h + (2 * bs * h if shared else 0) + 2 * bs * h + 12 * bs * k
-               + 4 * (e + 1))
+    rows_in = bs * k * (h + 4 * (h // 128)) if fp8_combine else 2 * bs * k * h
+    combine = rows_in + (2 * bs * h if shared else 0) + 2 * bs * h + 12 * bs * k + 4 * (e + 1)
     return {"layout": layout, "dispatch": dispatch, "combine": combine}
 
 
@@ -156,17 +158,22 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     cap = moe.moe_dispatch_capacity(w.bs, w.topk, w.experts, w.align)
-    inp = workloads.make(w, rows_y=None if w.identity_experts else cap)
+    fp8_combine = args.combine == "fp8"
+    inp = workloads.make(w, rows_y=None if (w.identity_experts or fp8_combine) else cap)
+    if fp8_combine:
+        yc, ys = workloads.e4m3_rows(cap, w.hidden, w.seed)
 
     nbytes = algorithmic_bytes(w.bs, w.hidden, w.experts, w.topk, inp["shared"] is not None,
-                               fp8=w.fp8)
+                               fp8=w.fp8, fp8_combine=fp8_combine)
     step_bytes = sum(nbytes.values())
     sets = args.sets or max(1, min(64, -(-(2 << 30) // step_bytes)))
 
     ids = torch.from_numpy(inp["expert_ids"]).to(dev)
     scales = torch.from_numpy(inp["expert_scales"]).to(dev)
     x0 = inp["x"].to(dev)
-    y0 = None if w.identity_experts else inp["y"].to(dev)
+    y0 = None if (w.identity_experts or fp8_combine) else inp["y"].to(dev)
+    yc0 = yc.to(dev) if fp8_combine else None
+    ys0 = ys.to(dev) if fp8_combine else None
     sh0 = None if inp["shared"] is None else inp["shared"].to(dev)
     bufs = []
     for i in range(sets):
@@ -175,6 +182,8 @@ def main():
         bufs.append({
             "x": x0 if i == 0 else x0.clone(),
             "y": ex if y0 is None else (y0 if i == 0 else y0.clone()),
+            "y_codes": None if yc0 is None else (yc0 if i == 0 else yc0.clone()),
+            "y_scales": None if ys0 is None else (ys0 if i == 0 else ys0.clone()),
             "scales": (torch.empty((cap, w.hidden // 128), dtype=torch.float32, device=dev)
                        if w.fp8 else None),
             "shared": None if sh0 is None else (sh0 if i == 0 else sh0.clone()),
@@ -189,6 +198,14 @@ def main():
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    def combine(b, lay):
+        if fp8_combine:
+            moe.moe_combine_fp8(b["y_codes"], b["y_scales"], ids, lay.expand_idx,
+                                lay.ep_send_counts, scales, b["shared"], w.experts, out=b["out"])
+        else:
+            moe.moe_combine(b["y"], ids, lay.expand_idx, lay.ep_send_counts, scales, b["shared"],
+                            w.experts, out=b["out"])
+
     def step(b, ev=None):
         lay = moe.moe_dispatch_layout(ids, w.experts, w.align, out=b["layout"], workspace=ws)
         moe.moe_dispatch(b["x"], ids, lay.expand_idx, lay.ep_send_counts, w.experts,
@@ -196,8 +213,7 @@ def main():
                          out_dtype="fp8" if w.fp8 else "bf16", quant_scales=b["scales"])
         if ev is not None:
             ev[0].record(stream)
-        moe.moe_combine(b["y"], ids, lay.expand_idx, lay.ep_send_counts, scales, b["shared"],
-                        w.experts, out=b["out"])
+        combine(b, lay)
         if ev is not None:
             ev[1].record(stream)
 
@@ -228,8 +244,7 @@ def main():
                          expand_x=b["expand_x"], capacity_rows=cap,
                          out_dtype="fp8" if w.fp8 else "bf16", quant_scales=b["scales"])
         e[2].record(stream)
-        moe.moe_combine(b["y"], ids, lay.expand_idx, lay.ep_send_counts, scales, b["shared"],
-                        w.experts, out=b["out"])
+        combine(b, lay)
         e[3].record(stream)
     torch.cuda.synchronize()
     lay_ms = [e[0].elapsed_time(e[1]) for e in brk]
@@ -242,7 +257,7 @@ def main():
 
     combine_s = mean(com_ms) / 1e3
     achieved = nbytes["combine"] / combine_s / 1e9
-    traffic = read_traffic(w.name)
+    traffic = None if fp8_combine else read_traffic(w.name)
     result = {
         "metric": METRIC,
         "value": round(step_bytes / (ms_per_step / 1e3) / 1e9, 2),
@@ -261,13 +276,14 @@ def main():
                    "topk": w.topk, "routing": w.routing + (f"(alpha={w.alpha})"
                                                            if w.routing == "zipf" else ""),
                    "align": w.align, "capacity_rows": cap, "buffer_sets": sets,
+                   "combine_input": "e4m3 + fp32 scales" if fp8_combine else "bf16",
                    "bytes_per_step": step_bytes},
         "kernels_ms": {"layout": round(mean(lay_ms), 4), "dispatch": round(mean(dis_ms), 4),
                        "combine": round(mean(com_ms), 4)},
         "kernels_gbs": {"layout": round(nbytes["layout"] / mean(lay_ms) / 1e6, 1),
                         "dispatch": round(nbytes["dispatch"] / mean(dis_ms) / 1e6, 1),
                         "combine": round(achieved, 1)},
-        "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "combine_fp8" if fp8_combine else "combine", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,

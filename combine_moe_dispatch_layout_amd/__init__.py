@@ -14,6 +14,8 @@ Entry points (same names as the C ABI):
   ``expand_x`` (and ``quant_scales`` for e4m3)
 * ``moe_combine(expand_x, expert_ids, expand_idx, ep_send_counts,
   expert_scales, shared_expert_x)`` -> ``x_out``
+* ``moe_combine_fp8(expand_x_codes, quant_scales, ...)`` -> ``x_out`` (expert
+  rows in the e4m3 + per-128-channel scale format, dequantised in the gather)
 * ``moe_dispatch_capacity`` / ``moe_dispatch_layout_workspace_size``
 """
 
@@ -28,7 +30,7 @@ import torch
 __all__ = [
     "MoeError", "Layout", "library_path", "load_library",
     "moe_dispatch_capacity", "moe_dispatch_layout_workspace_size",
-    "moe_dispatch_layout", "moe_dispatch", "moe_combine",
+    "moe_dispatch_layout", "moe_dispatch", "moe_combine", "moe_combine_fp8",
     "MOE_BF16", "MOE_FP8_E4M3", "MOE_FLAG_ID_RANGE", "MOE_FLAG_DUP_ID", "MOE_FLAG_GUARD",
 ]
 
@@ -73,6 +75,8 @@ def load_library() -> ctypes.CDLL:
                                         P, P, P]),
         "moe_combine": (ctypes.c_int, [P, i64, i64, P, P, P, P, P, i64, i32, i32, i32, i32, P,
                                        P, P]),
+        "moe_combine_fp8": (ctypes.c_int, [P, i64, i64, P, P, P, P, P, P, i64, i32, i32, i32,
+                                           i32, P, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -213,5 +217,38 @@ def moe_combine(expand_x: torch.Tensor, expert_ids: torch.Tensor, expand_idx: to
         _ptr(expand_x), _row_stride(expand_x, "expand_x"), cap, _ptr(expert_ids),
         _ptr(expand_idx), _ptr(ep_send_counts), _ptr(expert_scales), _ptr(shared_expert_x),
         shared_stride, bs, hidden, k, num_experts, _ptr(out), _ptr(status), _stream(expand_x))
+    _check(rc)
+    return out
+
+
+def moe_combine_fp8(expand_x: torch.Tensor, quant_scales: torch.Tensor, expert_ids: torch.Tensor,
+                    expand_idx: torch.Tensor, ep_send_counts: torch.Tensor,
+                    expert_scales: torch.Tensor, shared_expert_x: Optional[torch.Tensor],
+                    num_experts: int, *, out: Optional[torch.Tensor] = None,
+                    status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Combine over e4m3 expert rows (uint8 codes [cap, H]) with fp32 scales
+    [cap, H/128], each term dequantised before the weighted sum."""
+    _need(expand_x, torch.uint8, "expand_x", contiguous=False)
+    _need(quant_scales, torch.float32, "quant_scales")
+    _need(expert_ids, torch.int32, "expert_ids")
+    _need(expand_idx, torch.int32, "expand_idx")
+    _need(ep_send_counts, torch.int32, "ep_send_counts")
+    _need(expert_scales, torch.float32, "expert_scales")
+    bs, k = expert_ids.shape
+    cap, hidden = expand_x.shape
+    if quant_scales.shape != (cap, hidden // 128):
+        raise ValueError("quant_scales must be [capacity_rows, hidden/128]")
+    shared_stride = 0
+    if shared_expert_x is not None:
+        _need(shared_expert_x, torch.bfloat16, "shared_expert_x", contiguous=False)
+        shared_stride = _row_stride(shared_expert_x, "shared_expert_x")
+    if out is None:
+        out = torch.empty((bs, hidden), dtype=torch.bfloat16, device=expand_x.device)
+    _need(out, torch.bfloat16, "out")
+    rc = load_library().moe_combine_fp8(
+        _ptr(expand_x), _row_stride(expand_x, "expand_x"), cap, _ptr(quant_scales),
+        _ptr(expert_ids), _ptr(expand_idx), _ptr(ep_send_counts), _ptr(expert_scales),
+        _ptr(shared_expert_x), shared_stride, bs, hidden, k, num_experts, _ptr(out),
+        _ptr(status), _stream(expand_x))
     _check(rc)
     return out

@@ -148,4 +148,32 @@ int moe_combine(const void* expand_x, int64_t expand_x_stride, int64_t capacity_
                                         static_cast<hipStream_t>(stream)));
 }
 
+int moe_combine_fp8(const void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
+                    const float* quant_scales, const int32_t* expert_ids,
+                    const int32_t* expand_idx, const int32_t* ep_send_counts,
+                    const float* expert_scales, const void* shared_expert_x,
+                    int64_t shared_stride, int32_t bs, int32_t hidden, int32_t k,
+                    int32_t num_experts, void* x_out, int32_t* status, void* stream) {
+  if (!layout_args_ok(bs, k, num_experts, 1)) return MOE_ERR_INVALID_ARG;
+  if (hidden <= 0 || hidden % 128 != 0 || hidden > 65536) return MOE_ERR_INVALID_ARG;
+  if (capacity_rows < 0 || !rows_fit(bs, hidden)) return MOE_ERR_INVALID_ARG;
+  if (bs == 0) return MOE_OK;
+  if (expert_ids == nullptr || expand_idx == nullptr || ep_send_counts == nullptr ||
+      expert_scales == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (capacity_rows > 0) {
+    if (!row_ok(expand_x, expand_x_stride, hidden, 1)) return MOE_ERR_INVALID_ARG;
+    if (quant_scales == nullptr || (reinterpret_cast<uintptr_t>(quant_scales) & 3u) != 0)
+      return MOE_ERR_INVALID_ARG;
+  }
+  if (shared_expert_x != nullptr && !row_ok(shared_expert_x, shared_stride, hidden, 2))
+    return MOE_ERR_INVALID_ARG;
+  if (!row_ok(x_out, hidden, hidden, 2)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine_fp8(expand_x, expand_x_stride, capacity_rows,
+                                            quant_scales, expert_ids, expand_idx,
+                                            ep_send_counts, expert_scales, shared_expert_x,
+                                            shared_stride, bs, hidden, k, num_experts, x_out,
+                                            status, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -80,6 +80,86 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(
   }
 }
 
+// Quantised-transfer variant: expert rows are e4m3 codes with one fp32 scale
+// per 128 channels (the dispatch's e4m3 format).  Each thread owns 16
+// channels: per pair one 16-byte code load and one scale load (shared by the
+// 8 lanes of a scale block), decode with the hardware e4m3 -> fp32
+// conversion (exact), one fp32 multiply by the scale, then the same FMA chain,
+// shared row and bf16 rounding as the bf16 combine.
+template <int THREADS, int KMAX>
+__global__ __launch_bounds__(THREADS) void combine_fp8_kernel(
+    const u32x4* __restrict__ y, int64_t ys, const float* __restrict__ yscale, int32_t nblk,
+    int64_t cap, const int32_t* __restrict__ ids, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ send, const float* __restrict__ scales,
+    const u32x4* __restrict__ shared, int64_t ss, int32_t ngroups, int32_t nchunks, int32_t k,
+    int32_t E, u32x4* __restrict__ out, int32_t* status) {
+  __shared__ int send_lds[kMaxExperts + 1];
+  const int32_t t = blockIdx.x / nchunks;
+  const int32_t chunk = blockIdx.x - t * nchunks;
+  PairMeta meta;
+  fetch_pair_meta(meta, t, k, ids, idx, scales);
+  stage_send(send_lds, send, E);  // overlaps the fetch above
+  int64_t slot[KMAX];
+  float w[KMAX];
+  resolve_routes<KMAX>(meta, send_lds, k, E, cap, slot, w, status,
+                       threadIdx.x < kWave && chunk == 0);
+
+  const int32_t g = chunk * THREADS + threadIdx.x;  // 16-channel group
+  if (g >= ngroups) return;  // no workgroup barrier follows
+  u32x4 q[KMAX];
+  float s[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (slot[j] < 0) continue;
+    q[j] = load_stream(y + slot[j] * ys + g);
+    s[j] = yscale[slot[j] * nblk + (g >> 3)];
+  }
+  u32x4 sh0 = {0u, 0u, 0u, 0u}, sh1 = {0u, 0u, 0u, 0u};
+  if (shared) {
+    sh0 = load_stream(shared + (int64_t)t * ss + 2 * g);
+    sh1 = load_stream(shared + (int64_t)t * ss + 2 * g + 1);
+  }
+
+  float acc[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) acc[c] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (slot[j] < 0) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[j][c], false);  // bytes 0, 1
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[j][c], true);   // bytes 2, 3
+      const float d0 = lo[0] * s[j];
+      const float d1 = lo[1] * s[j];
+      const float d2 = hi[0] * s[j];
+      const float d3 = hi[1] * s[j];
+      acc[4 * c + 0] = __builtin_fmaf(w[j], d0, acc[4 * c + 0]);
+      acc[4 * c + 1] = __builtin_fmaf(w[j], d1, acc[4 * c + 1]);
+      acc[4 * c + 2] = __builtin_fmaf(w[j], d2, acc[4 * c + 2]);
+      acc[4 * c + 3] = __builtin_fmaf(w[j], d3, acc[4 * c + 3]);
+    }
+  }
+  if (shared) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      acc[2 * c] = acc[2 * c] + bf16lo_to_f32(sh0[c]);
+      acc[2 * c + 1] = acc[2 * c + 1] + bf16hi_to_f32(sh0[c]);
+      acc[8 + 2 * c] = acc[8 + 2 * c] + bf16lo_to_f32(sh1[c]);
+      acc[8 + 2 * c + 1] = acc[8 + 2 * c + 1] + bf16hi_to_f32(sh1[c]);
+    }
+  }
+  u32x4 o0, o1;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    o0[c] = f32_to_bf16_rne(acc[2 * c]) | (f32_to_bf16_rne(acc[2 * c + 1]) << 16);
+    o1[c] = f32_to_bf16_rne(acc[8 + 2 * c]) | (f32_to_bf16_rne(acc[8 + 2 * c + 1]) << 16);
+  }
+  u32x4* dst = out + (int64_t)t * (2 * (int64_t)ngroups) + 2 * g;
+  store_stream(o0, dst);
+  store_stream(o1, dst + 1);
+}
+
 template <int THREADS, int VPT>
 hipError_t launch_t(int kmax, dim3 grid, const u32x4* y, int64_t ys, int64_t cap,
                     const int32_t* ids, const int32_t* idx, const int32_t* send,
@@ -130,6 +210,51 @@ hipError_t launch_combine(const void* y, int64_t y_stride, int64_t capacity_rows
                                   static_cast<const u32x4*>(shared), shared_stride / 8, nvec,
                                   nchunks, k, num_experts, static_cast<u32x4*>(out),
                                   status, stream);
+}
+
+}  // namespace moe
+
+namespace moe {
+
+hipError_t launch_combine_fp8(const void* y, int64_t y_stride, int64_t capacity_rows,
+                              const float* y_scales, const int32_t* ids,
+                              const int32_t* expand_idx, const int32_t* send,
+                              const float* scales, const void* shared, int64_t shared_stride,
+                              int32_t bs, int32_t hidden, int32_t k, int32_t num_experts,
+                              void* out, int32_t* status, hipStream_t stream) {
+  constexpr int kThreads = MOE_COMBINE8_THREADS;
+  const int32_t ngroups = hidden / 16;
+  const int32_t nchunks = (ngroups + kThreads - 1) / kThreads;
+  const dim3 grid((uint32_t)(bs * nchunks));
+  const u32x4* yv = static_cast<const u32x4*>(y);
+  const u32x4* sv = static_cast<const u32x4*>(shared);
+  u32x4* ov = static_cast<u32x4*>(out);
+  const int64_t ys = y_stride / 16, ss = shared_stride / 8;
+  const int32_t nblk = hidden / 128;
+  const int kmax = k <= 2 ? 2 : k <= 4 ? 4 : k <= 8 ? 8 : 16;
+  switch (kmax) {
+    case 2:
+      combine_fp8_kernel<kThreads, 2><<<grid, kThreads, 0, stream>>>(
+          yv, ys, y_scales, nblk, capacity_rows, ids, expand_idx, send, scales, sv, ss, ngroups,
+          nchunks, k, num_experts, ov, status);
+      break;
+    case 4:
+      combine_fp8_kernel<kThreads, 4><<<grid, kThreads, 0, stream>>>(
+          yv, ys, y_scales, nblk, capacity_rows, ids, expand_idx, send, scales, sv, ss, ngroups,
+          nchunks, k, num_experts, ov, status);
+      break;
+    case 8:
+      combine_fp8_kernel<kThreads, 8><<<grid, kThreads, 0, stream>>>(
+          yv, ys, y_scales, nblk, capacity_rows, ids, expand_idx, send, scales, sv, ss, ngroups,
+          nchunks, k, num_experts, ov, status);
+      break;
+    default:
+      combine_fp8_kernel<kThreads, 16><<<grid, kThreads, 0, stream>>>(
+          yv, ys, y_scales, nblk, capacity_rows, ids, expand_idx, send, scales, sv, ss, ngroups,
+          nchunks, k, num_experts, ov, status);
+      break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -44,6 +44,9 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 #ifndef MOE_COMBINE_VPT
 #define MOE_COMBINE_VPT 1
 #endif
+#ifndef MOE_COMBINE8_THREADS
+#define MOE_COMBINE8_THREADS 64    // e4m3 combine: 16 channels per thread
+#endif
 #ifndef MOE_FP8_THREADS
 #define MOE_FP8_THREADS 256
 #endif
@@ -176,5 +179,12 @@ hipError_t launch_combine(const void* y, int64_t y_stride, int64_t capacity_rows
                           const float* scales, const void* shared, int64_t shared_stride,
                           int32_t bs, int32_t hidden, int32_t k, int32_t num_experts,
                           void* out, int32_t* status, hipStream_t stream);
+
+hipError_t launch_combine_fp8(const void* y, int64_t y_stride, int64_t capacity_rows,
+                              const float* y_scales, const int32_t* ids,
+                              const int32_t* expand_idx, const int32_t* send,
+                              const float* scales, const void* shared, int64_t shared_stride,
+                              int32_t bs, int32_t hidden, int32_t k, int32_t num_experts,
+                              void* out, int32_t* status, hipStream_t stream);
 
 }  // namespace moe

@@ -189,6 +189,34 @@ int moe_combine(const void* expand_x, int64_t expand_x_stride, int64_t capacity_
                 const void* shared_expert_x, int64_t shared_stride, int32_t bs, int32_t hidden,
                 int32_t k, int32_t num_experts, void* x_out, int32_t* status, void* stream);
 
+/*
+ * Quantised-transfer combine: the same weighted gather-sum as moe_combine,
+ * with the expert outputs in the e4m3 format that moe_dispatch emits (the
+ * combine page's comm_quant_mode names a quantised transfer on this path;
+ * its dtype is unreadable there, and this library reads it as that format).
+ *
+ *   x_out[t,h] = bf16( fma-chain_j( expert_scales[t,j],
+ *                         e4m3(expand_x[slot(t,j), h]) * quant_scales[slot(t,j), h/128] )
+ *                      + shared_expert_x[t,h] )
+ *
+ * Each term is dequantised with one fp32 multiply before the fused
+ * multiply-add chain over j ascending from +0; then the shared row is added
+ * and the sum rounded to nearest even into bf16.
+ *
+ *  expand_x       in  e4m3fn codes [capacity_rows, hidden], row stride
+ *                     expand_x_stride bytes (>= hidden, multiple of 16),
+ *                     16-byte aligned.
+ *  quant_scales   in  fp32 [capacity_rows, hidden/128] row-major.
+ *  hidden         in  a multiple of 128, <= 65536, bs*hidden/8 < 2^31.
+ *  other arguments as for moe_combine.
+ */
+int moe_combine_fp8(const void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
+                    const float* quant_scales, const int32_t* expert_ids,
+                    const int32_t* expand_idx, const int32_t* ep_send_counts,
+                    const float* expert_scales, const void* shared_expert_x,
+                    int64_t shared_stride, int32_t bs, int32_t hidden, int32_t k,
+                    int32_t num_experts, void* x_out, int32_t* status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -151,3 +151,19 @@ def test_combine_rules(lib):
     assert call(k=9) == 1
     assert call(cap=-5) == 1
     assert call(bs=0) == 0                 # empty batch: nothing to launch
+
+
+def test_combine_fp8_rules(lib):
+    def call(x=FAKE, xs=128, cap=64, qs=FAKE, h=128, sh=None, ss=0, out=FAKE, k=2):
+        return lib.moe_combine_fp8(x, xs, cap, qs, FAKE, FAKE, FAKE, FAKE, sh, ss, 4, h, k, 8,
+                                   out, None, None)
+
+    assert call(h=64, xs=64) == 1          # hidden must be a multiple of 128
+    assert call(qs=None) == 1              # scales required
+    assert call(qs=FAKE + 2) == 1          # misaligned scales
+    assert call(xs=120) == 1               # stride < hidden
+    assert call(x=FAKE + 8) == 1           # misaligned codes
+    assert call(sh=FAKE, ss=64) == 1       # shared stride < hidden
+    assert call(k=17) == 1
+    assert lib.moe_combine_fp8(FAKE, 128, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 0, 128, 2,
+                               8, FAKE, None, None) == 0   # empty batch

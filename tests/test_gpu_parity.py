@@ -430,3 +430,73 @@ def test_workload_full_size(name):
     if w.identity_experts:
         np.testing.assert_array_equal(oracle.bf16_bits_to_f32(host_bits(out)),
                                       oracle.bf16_bits_to_f32(workloads.bits(inp["x"])))
+
+
+# ------------------------------------------------------------------ e4m3 combine
+
+def run_combine_fp8(ids, codes, qs, scales, shared_bits, e, align):
+    moe = moe_mod()
+    c, s, r, _ = oracle.layout(ids, e, align)
+    sh = None if shared_bits is None else bf16_dev(shared_bits)
+    out = moe.moe_combine_fp8(dev(codes), dev(qs), dev(ids), dev(r), dev(s), dev(scales), sh, e)
+    torch.cuda.synchronize()
+    ref, _ = oracle.combine_fp8(codes, qs, ids, r, s, scales, shared_bits, e)
+    return host_bits(out), ref
+
+
+def test_combine_fp8_every_code():
+    """One-hot weights over rows holding each of the 256 codes, under a scale
+    that is not a power of two: exercises the hardware e4m3 decode of every
+    code (NaN codes included) against the oracle's decoder."""
+    hidden, e = 256, 256
+    codes = np.repeat(np.arange(256, dtype=np.uint8)[:, None], hidden, 1)
+    qs = np.tile(np.array([[0.37, 3.0e-3]], np.float32), (256, 1))
+    ids = np.arange(256, dtype=np.int32).reshape(256, 1)
+    got, ref = run_combine_fp8(ids, codes, qs, np.ones((256, 1), np.float32), None, e, 1)
+    gf, rf = oracle.bf16_bits_to_f32(got), oracle.bf16_bits_to_f32(ref)
+    nan = np.isnan(rf)
+    assert np.array_equal(np.isnan(gf), nan)
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("bs,h,e,k,shared", [(1, 128, 1, 1, False), (16, 128, 8, 2, False),
+                                             (77, 1152, 40, 5, True), (300, 4096, 256, 8, True),
+                                             (65, 7168, 64, 16, True)])
+def test_combine_fp8_every_element(bs, h, e, k, shared):
+    rng = np.random.default_rng(bs * 11 + k)
+    ids = random_ids(rng, bs, e, k)
+    cap = oracle.capacity(bs, k, e, 128)
+    codes_t, qs_t = workloads.e4m3_rows(cap, h, seed=bs)
+    codes, qs = codes_t.numpy(), qs_t.numpy()
+    sc = workloads.scales(bs, k, seed=bs)
+    sh = random_bf16(rng, (bs, h)) if shared else None
+    got, ref = run_combine_fp8(ids, codes, qs, sc, sh, e, 128)
+    assert ulp_diff(got, ref).max() <= 1
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_fp8_round_trip_on_gpu():
+    """e4m3 dispatch -> e4m3 combine with identity experts: matches the
+    oracle's own round trip bit for bit."""
+    moe = moe_mod()
+    w = workloads.WORKLOADS["fp8"]
+    inp = workloads.make(w)
+    ids, sc = inp["expert_ids"], inp["expert_scales"]
+    ids_d = dev(ids)
+    lay = moe.moe_dispatch_layout(ids_d, w.experts, w.align)
+    codes, qs = moe.moe_dispatch(inp["x"].to(DEV), ids_d, lay.expand_idx, lay.ep_send_counts,
+                                 w.experts, out_dtype="fp8")
+    out = moe.moe_combine_fp8(codes, qs, ids_d, lay.expand_idx, lay.ep_send_counts, dev(sc),
+                              None, w.experts)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    sample = np.unique(rng.integers(0, w.bs, 48))
+    c, s, r, _ = oracle.layout(ids, w.experts, w.align)
+    cap = oracle.capacity(w.bs, w.topk, w.experts, w.align)
+    x_bits = workloads.bits(inp["x"])
+    # the oracle's e4m3 rows for the sampled tokens only, at their own slots
+    sub_ids = ids[sample]
+    sub_r = r.reshape(w.bs, w.topk)[sample].ravel()
+    rc, rq, _ = oracle.dispatch_fp8(x_bits[sample], sub_ids, sub_r, s, w.experts, cap)
+    ref, _ = oracle.combine_fp8(rc, rq, sub_ids, sub_r, s, sc[sample], None, w.experts)
+    np.testing.assert_array_equal(host_bits(out[torch.from_numpy(sample).to(DEV)]), ref)

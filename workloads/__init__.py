@@ -118,6 +118,23 @@ def bf16_rows(rows: int, cols: int, seed: int, stream: str = "x") -> torch.Tenso
     return out
 
 
+def e4m3_rows(rows: int, cols: int, seed: int, stream: str = "y"):
+    """Expert-output rows in e4m3 form: uint8 codes [rows, cols] and fp32
+    scales [rows, cols/128].  Codes are N(0,1)*64 values cast to float8_e4m3fn
+    by torch (saturating to +-448); scales are U(1e-3, 2e-2).  The values are
+    only realistic-looking inputs; no quantisation rule of the method is used."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(_torch_seed(seed_streams(seed)[stream]) ^ 0x5DEECE66D)
+    codes = torch.empty((rows, cols), dtype=torch.uint8)
+    step = max(1, CHUNK_ELEMS // max(cols, 1))
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        v = torch.randn((r1 - r0, cols), generator=gen, dtype=torch.float32) * 64.0
+        codes[r0:r1] = v.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    scales = torch.rand((rows, cols // 128), generator=gen, dtype=torch.float32) * 0.019 + 0.001
+    return codes, scales
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """uint16 bit patterns of a CPU bfloat16 tensor (a view, no copy)."""
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
