@@ -16,6 +16,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libmoe_dispatch.so")
 SOURCES = ["api.hip", "layout.hip", "dispatch.hip", "combine.hip"]
 ARCH = "gfx950"
@@ -40,7 +41,7 @@ def _obj_dir() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(_obj_dir(), os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, f"-I{INCLUDE}", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -85,9 +85,12 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(
 // channels: per pair one 16-byte code load and one scale load (shared by the
 // 8 lanes of a scale block), decode with the hardware e4m3 -> fp32
 // conversion (exact), one fp32 multiply by the scale, then the same FMA chain,
-// shared row and bf16 rounding as the bf16 combine.
-template <int THREADS, int KMAX>
-__global__ __launch_bounds__(THREADS) void combine_fp8_kernel(
+// shared row and bf16 rounding as the bf16 combine.  One workgroup spans a
+// whole row when it fits (up to 1024 threads), so each scale
+// row is fetched by one compute unit instead of by one per chunk (measured:
+// 66.4 -> 62.2 us at H = 7168 against 64-thread workgroups).
+template <int KMAX>
+__global__ __launch_bounds__(1024) void combine_fp8_kernel(
     const u32x4* __restrict__ y, int64_t ys, const float* __restrict__ yscale, int32_t nblk,
     int64_t cap, const int32_t* __restrict__ ids, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ send, const float* __restrict__ scales,
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(THREADS) void combine_fp8_kernel(
   resolve_routes<KMAX>(meta, send_lds, k, E, cap, slot, w, status,
                        threadIdx.x < kWave && chunk == 0);
 
-  const int32_t g = chunk * THREADS + threadIdx.x;  // 16-channel group
+  const int32_t g = chunk * (int32_t)blockDim.x + threadIdx.x;  // 16-channel group
   if (g >= ngroups) return;  // no workgroup barrier follows
   u32x4 q[KMAX];
   float s[KMAX];
@@ -222,9 +225,9 @@ hipError_t launch_combine_fp8(const void* y, int64_t y_stride, int64_t capacity_
                               const float* scales, const void* shared, int64_t shared_stride,
                               int32_t bs, int32_t hidden, int32_t k, int32_t num_experts,
                               void* out, int32_t* status, hipStream_t stream) {
-  constexpr int kThreads = MOE_COMBINE8_THREADS;
   const int32_t ngroups = hidden / 16;
-  const int32_t nchunks = (ngroups + kThreads - 1) / kThreads;
+  const int32_t threads = ngroups <= 1024 ? (ngroups + kWave - 1) / kWave * kWave : 1024;
+  const int32_t nchunks = (ngroups + threads - 1) / threads;
   const dim3 grid((uint32_t)(bs * nchunks));
   const u32x4* yv = static_cast<const u32x4*>(y);
   const u32x4* sv = static_cast<const u32x4*>(shared);
@@ -234,22 +237,22 @@ hipError_t launch_combine_fp8(const void* y, int64_t y_stride, int64_t capacity_
   const int kmax = k <= 2 ? 2 : k <= 4 ? 4 : k <= 8 ? 8 : 16;
   switch (kmax) {
     case 2:
-      combine_fp8_kernel<kThreads, 2><<<grid, kThreads, 0, stream>>>(
+      combine_fp8_kernel<2><<<grid, threads, 0, stream>>>(
           yv, ys, y_scales, nblk, capacity_rows, ids, expand_idx, send, scales, sv, ss, ngroups,
           nchunks, k, num_experts, ov, status);
       break;
     case 4:
-      combine_fp8_kernel<kThreads, 4><<<grid, kThreads, 0, stream>>>(
+      combine_fp8_kernel<4><<<grid, threads, 0, stream>>>(
           yv, ys, y_scales, nblk, capacity_rows, ids, expand_idx, send, scales, sv, ss, ngroups,
           nchunks, k, num_experts, ov, status);
       break;
     case 8:
-      combine_fp8_kernel<kThreads, 8><<<grid, kThreads, 0, stream>>>(
+      combine_fp8_kernel<8><<<grid, threads, 0, stream>>>(
           yv, ys, y_scales, nblk, capacity_rows, ids, expand_idx, send, scales, sv, ss, ngroups,
           nchunks, k, num_experts, ov, status);
       break;
     default:
-      combine_fp8_kernel<kThreads, 16><<<grid, kThreads, 0, stream>>>(
+      combine_fp8_kernel<16><<<grid, threads, 0, stream>>>(
           yv, ys, y_scales, nblk, capacity_rows, ids, expand_idx, send, scales, sv, ss, ngroups,
           nchunks, k, num_experts, ov, status);
       break;

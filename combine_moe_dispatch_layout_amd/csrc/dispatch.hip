@@ -109,12 +109,17 @@ __global__ __launch_bounds__(THREADS) void dispatch_fp8_kernel(
     }
   }
 
+  // Code rows are written with streaming stores (each wave covers whole
+  // lines).  A wave holds only 32 bytes of a scale row, so scale stores stay
+  // ordinary cached stores: L2 merges the pieces of a line before it is
+  // written back, where streaming partial-line writes would each reach HBM
+  // (measured: 58.5 -> 48.6 us on the 4096-token e4m3 dispatch).
   const bool writes_scale = active && (g & 7) == 0;
 #pragma unroll
   for (int jj = 0; jj < KMAX; ++jj) {
     if (slot[jj] < 0) continue;
     if (active) store_stream(codes, out + slot[jj] * os + g);
-    if (writes_scale) store_stream(s, scales + slot[jj] * nblk + (g >> 3));
+    if (writes_scale) scales[slot[jj] * nblk + (g >> 3)] = s;
   }
 }
 

@@ -6,7 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/moe_dispatch.h"
+#include "moe_dispatch.h"  // include/ (on the include path)
 
 namespace moe {
 
@@ -43,9 +43,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 #endif
 #ifndef MOE_COMBINE_VPT
 #define MOE_COMBINE_VPT 1
-#endif
-#ifndef MOE_COMBINE8_THREADS
-#define MOE_COMBINE8_THREADS 64    // e4m3 combine: 16 channels per thread
 #endif
 #ifndef MOE_FP8_THREADS
 #define MOE_FP8_THREADS 256
