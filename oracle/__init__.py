@@ -20,6 +20,9 @@ expert_scales / shared_expert_x; TEMPO summary section 1 for the 128-row tile):
   unweighted shared row, rounded to bf16 (nearest-even).
 * ``combine_fp8`` -- the same sum over e4m3 expert rows, each term dequantised
   as ``e4m3_value * scale`` (one binary32 multiply) first.
+* ``layout_replicated`` -- each pair picks a physical replica of its expert
+  by a SplitMix64 draw against cumulative thresholds (TEMPO summary, section
+  2, system integration), then the layout runs over the replicas.
 
 Parity status: every function is pinned by the ``not gpu`` tests (brute force,
 closed forms, invariants, library codecs); none is "parity unpinned".
@@ -46,6 +49,7 @@ ERR_UNSUPPORTED = 3
 FLAG_ID_RANGE = 1
 FLAG_DUP_ID = 2
 FLAG_GUARD = 4
+FLAG_REPLICA = 8
 
 # Sentinel the oracle's dispatch buffers are prefilled with, so that rows the
 # method leaves unwritten (padding) stay recognisable.
@@ -96,6 +100,9 @@ def _load():
                                           P, P]),
         "oracle_combine_fp8": (ctypes.c_int, [P, i64, i64, P, P, P, P, P, P, i64, i32, i32,
                                               i32, i32, P, P]),
+        "oracle_splitmix64": (ctypes.c_uint64, [ctypes.c_uint64, ctypes.c_uint64]),
+        "oracle_layout_replicated": (ctypes.c_int, [P, i32, i32, i32, P, P, i32, ctypes.c_uint64,
+                                                    i32, P, P, P, P, P]),
         "oracle_f32_to_bf16_array": (None, [P, i64, P]),
         "oracle_f32_to_e4m3_array": (None, [P, i64, P]),
         "oracle_e4m3_to_f32_array": (None, [P, i64, P]),
@@ -282,3 +289,30 @@ def combine_fp8(y_codes: np.ndarray, y_scales: np.ndarray, expert_ids: np.ndarra
     if rc != OK:
         raise OracleArgError(rc)
     return out, int(flags[0])
+
+
+def splitmix64(seed: int, i: int) -> int:
+    """Draw ``i`` of the SplitMix64 stream seeded with ``seed``."""
+    return int(_load().oracle_splitmix64(seed & 0xFFFFFFFFFFFFFFFF, i))
+
+
+def layout_replicated(expert_ids: np.ndarray, num_experts: int, replica_offsets: np.ndarray,
+                      replica_thresholds: np.ndarray, seed: int, align: int = 128):
+    """Returns ``(replica_ids[BS,K], replica_counts[P], ep_send_counts[P+1],
+    expand_idx[BS*K], flags)``."""
+    ids = _i32(expert_ids)
+    bs, k = ids.shape
+    off = _i32(replica_offsets)
+    thr = np.ascontiguousarray(replica_thresholds, dtype=np.uint32)
+    p = thr.size
+    rep = np.zeros((bs, k), np.int32)
+    counts = np.zeros(p, np.int32)
+    send = np.zeros(p + 1, np.int32)
+    idx = np.zeros(bs * k, np.int32)
+    flags = np.zeros(1, np.int32)
+    rc = _load().oracle_layout_replicated(_ptr(ids), bs, k, num_experts, _ptr(off), _ptr(thr), p,
+                                          seed & 0xFFFFFFFFFFFFFFFF, align, _ptr(rep),
+                                          _ptr(counts), _ptr(send), _ptr(idx), _ptr(flags))
+    if rc != OK:
+        raise OracleArgError(rc)
+    return rep, counts, send, idx, int(flags[0])

@@ -416,6 +416,75 @@ int oracle_combine_fp8(const uint8_t* y, int64_t y_stride, int64_t capacity_rows
 }
 
 /* ------------------------------------------------------------------------ */
+/* Replica-aware dispatch (TEMPO summary, section 2, system integration: one  */
+/* in-graph kernel does the probabilistic replica choice and the counting).  */
+/* ------------------------------------------------------------------------ */
+
+/* SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+ * generators", OOPSLA 2014): the generator's state advances by the golden
+ * gamma 0x9E3779B97F4A7C15 per draw and each state is finalised by the
+ * variant-13 mixer.  Draw i (0-based) of the stream seeded with `seed` is the
+ * finalised state seed + (i+1)*gamma, so any draw can be computed directly
+ * from its counter. */
+uint64_t oracle_splitmix64(uint64_t seed, uint64_t i) {
+    uint64_t z = seed + (i + 1u) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+#define ORC_FLAG_REPLICA 8
+
+/* Each valid pair (t, j) with logical expert e draws u = the upper 32 bits of
+ * draw t*K+j of the SplitMix64 stream, and goes to the first replica r of e
+ * (r in [replica_offsets[e], replica_offsets[e+1])) whose cumulative
+ * threshold satisfies u <= replica_thresholds[r].  A logical id outside
+ * [0, E), or an expert whose thresholds never reach u (an empty or malformed
+ * range), gives -1 (the latter also ORC_FLAG_REPLICA).  Then the ordinary
+ * layout runs over the num_replicas physical replicas. */
+int oracle_layout_replicated(const int32_t* expert_ids, int32_t bs, int32_t k,
+                             int32_t num_experts, const int32_t* replica_offsets,
+                             const uint32_t* replica_thresholds, int32_t num_replicas,
+                             uint64_t seed, int32_t align, int32_t* replica_ids,
+                             int32_t* replica_counts, int32_t* ep_send_counts,
+                             int32_t* expand_idx, int32_t* flags) {
+    int rc = oracle_check_layout_args(bs, k, num_experts, align);
+    if (rc == ORC_OK) rc = oracle_check_layout_args(bs, k, num_replicas, align);
+    if (rc != ORC_OK) return rc;
+    int32_t f = 0;
+    for (int32_t t = 0; t < bs; ++t)
+        for (int32_t j = 0; j < k; ++j) {
+            int64_t i = (int64_t)t * k + j;
+            int32_t e = expert_ids[i];
+            replica_ids[i] = -1;
+            if (e < 0 || e >= num_experts) {
+                f |= ORC_FLAG_ID_RANGE;
+                continue;
+            }
+            for (int32_t j2 = 0; j2 < j; ++j2)
+                if (expert_ids[(int64_t)t * k + j2] == e) f |= ORC_FLAG_DUP_ID;
+            uint32_t u = (uint32_t)(oracle_splitmix64(seed, (uint64_t)i) >> 32);
+            int32_t lo = replica_offsets[e], hi = replica_offsets[e + 1];
+            int32_t chosen = -1;
+            for (int32_t r = lo; r < hi; ++r)
+                if (r >= 0 && r < num_replicas && u <= replica_thresholds[r]) {
+                    chosen = r;
+                    break;
+                }
+            if (chosen < 0) f |= ORC_FLAG_REPLICA;
+            replica_ids[i] = chosen;
+        }
+    int32_t f2 = 0;
+    rc = oracle_layout(replica_ids, bs, k, num_replicas, align, replica_counts, ep_send_counts,
+                       expand_idx, &f2);
+    if (rc != ORC_OK) return rc;
+    /* -1 replica ids were already accounted for above; repeated replicas in a
+     * row can only come from repeated logical experts */
+    if (flags) *flags = f;
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Array forms of the codecs, so the tests can sweep whole code spaces.      */
 /* ------------------------------------------------------------------------ */
 
