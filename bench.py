@@ -46,6 +46,9 @@ def parse():
                    choices=["tiny", "decode", "skewed", "fp8", "large"])
     p.add_argument("--combine", default="bf16", choices=["bf16", "fp8"],
                    help="expert-output format read by the combine (fp8 = e4m3 + scales)")
+    p.add_argument("--replicas", type=int, default=0,
+                   help="split the N most popular experts into 4 replicas each and use the "
+                        "replica-aware layout (probabilistic replica choice + count gathering)")
     p.add_argument("--sets", type=int, default=0,
                    help="buffer sets rotated across steps (0 = enough to exceed 2 GiB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -157,13 +160,22 @@ def main():
     w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    cap = moe.moe_dispatch_capacity(w.bs, w.topk, w.experts, w.align)
+    n_phys = w.experts
+    rep_off = rep_thr = None
+    if args.replicas > 0:
+        hot = workloads.popularity(w.experts, w.routing, w.seed)[:args.replicas]
+        off_np, thr_np = workloads.replica_plan(w.experts, hot, 4)
+        n_phys = int(off_np[-1])
+        rep_off = torch.from_numpy(off_np).to(dev)
+        rep_thr = torch.from_numpy(thr_np.view("int32")).to(dev)
+        rep_ids = torch.empty((w.bs, w.topk), dtype=torch.int32, device=dev)
+    cap = moe.moe_dispatch_capacity(w.bs, w.topk, n_phys, w.align)
     fp8_combine = args.combine == "fp8"
     inp = workloads.make(w, rows_y=None if (w.identity_experts or fp8_combine) else cap)
     if fp8_combine:
         yc, ys = workloads.e4m3_rows(cap, w.hidden, w.seed)
 
-    nbytes = algorithmic_bytes(w.bs, w.hidden, w.experts, w.topk, inp["shared"] is not None,
+    nbytes = algorithmic_bytes(w.bs, w.hidden, n_phys, w.topk, inp["shared"] is not None,
                                fp8=w.fp8, fp8_combine=fp8_combine)
     step_bytes = sum(nbytes.values())
     sets = args.sets or max(1, min(64, -(-(2 << 30) // step_bytes)))
@@ -189,28 +201,40 @@ def main():
             "shared": None if sh0 is None else (sh0 if i == 0 else sh0.clone()),
             "expand_x": ex,
             "out": torch.empty((w.bs, w.hidden), dtype=torch.bfloat16, device=dev),
-            "layout": moe.Layout(torch.empty(w.experts, dtype=torch.int32, device=dev),
-                                 torch.empty(w.experts + 1, dtype=torch.int32, device=dev),
+            "layout": moe.Layout(torch.empty(n_phys, dtype=torch.int32, device=dev),
+                                 torch.empty(n_phys + 1, dtype=torch.int32, device=dev),
                                  torch.empty(w.bs * w.topk, dtype=torch.int32, device=dev),
                                  torch.empty(1, dtype=torch.int32, device=dev)),
         })
-    ws_bytes = moe.moe_dispatch_layout_workspace_size(w.bs, w.topk, w.experts)
+    ws_bytes = moe.moe_dispatch_layout_workspace_size(w.bs, w.topk, n_phys)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def combine(b, lay):
-        if fp8_combine:
-            moe.moe_combine_fp8(b["y_codes"], b["y_scales"], ids, lay.expand_idx,
-                                lay.ep_send_counts, scales, b["shared"], w.experts, out=b["out"])
-        else:
-            moe.moe_combine(b["y"], ids, lay.expand_idx, lay.ep_send_counts, scales, b["shared"],
-                            w.experts, out=b["out"])
+    route_ids = rep_ids if args.replicas > 0 else ids
 
-    def step(b, ev=None):
-        lay = moe.moe_dispatch_layout(ids, w.experts, w.align, out=b["layout"], workspace=ws)
-        moe.moe_dispatch(b["x"], ids, lay.expand_idx, lay.ep_send_counts, w.experts,
+    def layout(b):
+        if args.replicas > 0:
+            return moe.moe_dispatch_layout_replicated(
+                ids, w.experts, rep_off, rep_thr, 1234, w.align, out=b["layout"],
+                replica_ids=rep_ids, workspace=ws)[1]
+        return moe.moe_dispatch_layout(ids, w.experts, w.align, out=b["layout"], workspace=ws)
+
+    def dispatch(b, lay):
+        moe.moe_dispatch(b["x"], route_ids, lay.expand_idx, lay.ep_send_counts, n_phys,
                          expand_x=b["expand_x"], capacity_rows=cap,
                          out_dtype="fp8" if w.fp8 else "bf16", quant_scales=b["scales"])
+
+    def combine(b, lay):
+        if fp8_combine:
+            moe.moe_combine_fp8(b["y_codes"], b["y_scales"], route_ids, lay.expand_idx,
+                                lay.ep_send_counts, scales, b["shared"], n_phys, out=b["out"])
+        else:
+            moe.moe_combine(b["y"], route_ids, lay.expand_idx, lay.ep_send_counts, scales,
+                            b["shared"], n_phys, out=b["out"])
+
+    def step(b, ev=None):
+        lay = layout(b)
+        dispatch(b, lay)
         if ev is not None:
             ev[0].record(stream)
         combine(b, lay)
@@ -238,11 +262,9 @@ def main():
     for i, e in enumerate(brk):
         b = bufs[i % sets]
         e[0].record(stream)
-        lay = moe.moe_dispatch_layout(ids, w.experts, w.align, out=b["layout"], workspace=ws)
+        lay = layout(b)
         e[1].record(stream)
-        moe.moe_dispatch(b["x"], ids, lay.expand_idx, lay.ep_send_counts, w.experts,
-                         expand_x=b["expand_x"], capacity_rows=cap,
-                         out_dtype="fp8" if w.fp8 else "bf16", quant_scales=b["scales"])
+        dispatch(b, lay)
         e[2].record(stream)
         combine(b, lay)
         e[3].record(stream)
@@ -257,7 +279,7 @@ def main():
 
     combine_s = mean(com_ms) / 1e3
     achieved = nbytes["combine"] / combine_s / 1e9
-    traffic = None if fp8_combine else read_traffic(w.name)
+    traffic = None if (fp8_combine or args.replicas > 0) else read_traffic(w.name)
     result = {
         "metric": METRIC,
         "value": round(step_bytes / (ms_per_step / 1e3) / 1e9, 2),
@@ -277,6 +299,8 @@ def main():
                                                            if w.routing == "zipf" else ""),
                    "align": w.align, "capacity_rows": cap, "buffer_sets": sets,
                    "combine_input": "e4m3 + fp32 scales" if fp8_combine else "bf16",
+                   "replicas": ({"hot_experts": args.replicas, "per_hot": 4,
+                                 "physical": n_phys} if args.replicas > 0 else None),
                    "bytes_per_step": step_bytes},
         "kernels_ms": {"layout": round(mean(lay_ms), 4), "dispatch": round(mean(dis_ms), 4),
                        "combine": round(mean(com_ms), 4)},

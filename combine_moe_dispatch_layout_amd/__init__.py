@@ -16,6 +16,8 @@ Entry points (same names as the C ABI):
   expert_scales, shared_expert_x)`` -> ``x_out``
 * ``moe_combine_fp8(expand_x_codes, quant_scales, ...)`` -> ``x_out`` (expert
   rows in the e4m3 + per-128-channel scale format, dequantised in the gather)
+* ``moe_dispatch_layout_replicated(expert_ids, num_experts, replica_offsets,
+  replica_thresholds, seed)`` -> ``(replica_ids, Layout over replicas)``
 * ``moe_dispatch_capacity`` / ``moe_dispatch_layout_workspace_size``
 """
 
@@ -30,7 +32,8 @@ import torch
 __all__ = [
     "MoeError", "Layout", "library_path", "load_library",
     "moe_dispatch_capacity", "moe_dispatch_layout_workspace_size",
-    "moe_dispatch_layout", "moe_dispatch", "moe_combine", "moe_combine_fp8",
+    "moe_dispatch_layout", "moe_dispatch_layout_replicated", "moe_dispatch", "moe_combine",
+    "moe_combine_fp8",
     "MOE_BF16", "MOE_FP8_E4M3", "MOE_FLAG_ID_RANGE", "MOE_FLAG_DUP_ID", "MOE_FLAG_GUARD",
 ]
 
@@ -39,7 +42,7 @@ _LIB_PATH = os.path.join(_HERE, "libmoe_dispatch.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = range(5)
 MOE_BF16, MOE_FP8_E4M3 = 0, 1
-MOE_FLAG_ID_RANGE, MOE_FLAG_DUP_ID, MOE_FLAG_GUARD = 1, 2, 4
+MOE_FLAG_ID_RANGE, MOE_FLAG_DUP_ID, MOE_FLAG_GUARD, MOE_FLAG_REPLICA = 1, 2, 4, 8
 
 _lib = None
 
@@ -77,6 +80,9 @@ def load_library() -> ctypes.CDLL:
                                        P, P]),
         "moe_combine_fp8": (ctypes.c_int, [P, i64, i64, P, P, P, P, P, P, i64, i32, i32, i32,
                                            i32, P, P, P]),
+        "moe_dispatch_layout_replicated": (ctypes.c_int, [P, i32, i32, i32, P, P, i32,
+                                                          ctypes.c_uint64, i32, P, P, P, P, P, P,
+                                                          sz, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -252,3 +258,40 @@ def moe_combine_fp8(expand_x: torch.Tensor, quant_scales: torch.Tensor, expert_i
         _ptr(status), _stream(expand_x))
     _check(rc)
     return out
+
+
+def moe_dispatch_layout_replicated(expert_ids: torch.Tensor, num_experts: int,
+                                   replica_offsets: torch.Tensor,
+                                   replica_thresholds: torch.Tensor, seed: int,
+                                   align: int = 128, *, out: Optional[Layout] = None,
+                                   replica_ids: Optional[torch.Tensor] = None,
+                                   workspace: Optional[torch.Tensor] = None):
+    """Choose a physical replica per pair (SplitMix64 draw against cumulative
+    uint32 thresholds, given as int32 or uint32 bit patterns) and lay the
+    pairs out over the replicas.  Returns ``(replica_ids [BS, K], Layout)``."""
+    _need(expert_ids, torch.int32, "expert_ids")
+    _need(replica_offsets, torch.int32, "replica_offsets")
+    if replica_thresholds.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("replica_thresholds must hold uint32 bit patterns (int32 or uint32)")
+    _need(replica_thresholds, replica_thresholds.dtype, "replica_thresholds")
+    bs, k = expert_ids.shape
+    p = replica_thresholds.numel()
+    dev = expert_ids.device
+    if out is None:
+        out = Layout(torch.empty(p, dtype=torch.int32, device=dev),
+                     torch.empty(p + 1, dtype=torch.int32, device=dev),
+                     torch.empty(bs * k, dtype=torch.int32, device=dev),
+                     torch.empty(1, dtype=torch.int32, device=dev))
+    if replica_ids is None:
+        replica_ids = torch.empty((bs, k), dtype=torch.int32, device=dev)
+    ws_bytes = moe_dispatch_layout_workspace_size(bs, k, p)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    rc = load_library().moe_dispatch_layout_replicated(
+        _ptr(expert_ids), bs, k, num_experts, _ptr(replica_offsets), _ptr(replica_thresholds), p,
+        seed & 0xFFFFFFFFFFFFFFFF, align, _ptr(replica_ids), _ptr(out.expert_counts),
+        _ptr(out.ep_send_counts), _ptr(out.expand_idx), _ptr(out.status), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(expert_ids))
+    _check(rc)
+    return replica_ids, out

@@ -92,6 +92,35 @@ int moe_dispatch_layout(const int32_t* expert_ids, int32_t bs, int32_t k, int32_
     return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_layout(expert_ids, k, num_experts, align, plan, expert_counts,
                                        ep_send_counts, expand_idx, status, workspace,
+                                       moe::ReplicaMap{}, static_cast<hipStream_t>(stream)));
+}
+
+int moe_dispatch_layout_replicated(const int32_t* expert_ids, int32_t bs, int32_t k,
+                                   int32_t num_experts, const int32_t* replica_offsets,
+                                   const uint32_t* replica_thresholds, int32_t num_replicas,
+                                   uint64_t seed, int32_t align, int32_t* replica_ids,
+                                   int32_t* replica_counts, int32_t* ep_send_counts,
+                                   int32_t* expand_idx, int32_t* status, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!layout_args_ok(bs, k, num_experts, align)) return MOE_ERR_INVALID_ARG;
+  if (!layout_args_ok(bs, k, num_replicas, align)) return MOE_ERR_INVALID_ARG;
+  if (replica_counts == nullptr || ep_send_counts == nullptr || replica_offsets == nullptr ||
+      replica_thresholds == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (bs > 0 && (expert_ids == nullptr || expand_idx == nullptr || replica_ids == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  const moe::LayoutPlan plan = moe::plan_layout(bs, k);
+  const size_t need = moe::layout_workspace_bytes(plan, num_replicas);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return MOE_ERR_WORKSPACE;
+  moe::ReplicaMap map;
+  map.offsets = replica_offsets;
+  map.thresholds = replica_thresholds;
+  map.n_logical = num_experts;
+  map.seed = seed;
+  map.out = replica_ids;
+  return hip_status(moe::launch_layout(expert_ids, k, num_replicas, align, plan, replica_counts,
+                                       ep_send_counts, expand_idx, status, workspace, map,
                                        static_cast<hipStream_t>(stream)));
 }
 

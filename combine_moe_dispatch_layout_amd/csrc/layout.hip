@@ -88,16 +88,36 @@ __device__ __forceinline__ int duplicate_flags(const int32_t* __restrict__ ids, 
   return fl;
 }
 
+// SplitMix64 draw i of the stream seeded with `seed` (Steele, Lea and Flood,
+// OOPSLA 2014): the state seed + (i+1)*golden-gamma through the variant-13
+// finaliser.  Counter-based, so every pair computes its own draw.
+__device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t i) {
+  uint64_t z = seed + (i + 1u) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Ranking over E "experts".  With a replica map, ids are logical experts in
+// [0, map.n_logical) and each pair is first sent to one of its expert's
+// physical replicas (E = number of replicas): u = upper 32 bits of the pair's
+// SplitMix64 draw, replica = first r of the expert's range with
+// u <= thresholds[r] (TEMPO summary, section 2: probabilistic replica
+// dispatch and count gathering in one in-graph kernel).
 template <int R>
 __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     const int32_t* __restrict__ ids, int32_t n_pairs, int32_t k, int32_t E, int32_t align,
     int32_t* __restrict__ expand_idx, int32_t* __restrict__ block_hist,
     int32_t* __restrict__ block_flags, int32_t* __restrict__ counts, int32_t* __restrict__ send,
-    int32_t* __restrict__ status) {
+    int32_t* __restrict__ status, ReplicaMap map) {
   __shared__ unsigned long long mask[kLayoutWaves][kMaxExperts];  // 32 KB
   __shared__ int wave_run[kLayoutWaves][kMaxExperts];             // 16 KB
+  __shared__ int rep_off[kMaxExperts + 1];
+  __shared__ uint32_t rep_thr[kMaxExperts];
   __shared__ int wave_tot[kLayoutWaves];
   __shared__ int flags_lds;
+  const bool mapped = map.offsets != nullptr;
+  const int32_t n_ids = mapped ? map.n_logical : E;  // valid range of the input ids
 
   constexpr int kPairs = kLayoutThreads * R;
   const int tid = threadIdx.x;
@@ -120,8 +140,35 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     (&wave_run[0][0])[j] = 0;
   }
   if (tid == 0) flags_lds = 0;
-  int fl = duplicate_flags(ids, k, E, begin, end);
+  if (mapped) {
+    for (int j = tid; j <= n_ids; j += kLayoutThreads) rep_off[j] = map.offsets[j];
+    for (int j = tid; j < E; j += kLayoutThreads) rep_thr[j] = map.thresholds[j];
+  }
+  int fl = duplicate_flags(ids, k, n_ids, begin, end);
   __syncthreads();
+
+  if (mapped) {
+#pragma unroll
+    for (int s = 0; s < R; ++s) {
+      const int i = wbase + s * kWave + lane;
+      if (i >= end) continue;
+      int r = -1;
+      if (e[s] >= 0 && e[s] < n_ids) {
+        const uint32_t u = (uint32_t)(splitmix64(map.seed, (uint64_t)i) >> 32);
+        const int lo = rep_off[e[s]], hi = rep_off[e[s] + 1];
+        for (int c = lo; c < hi; ++c)
+          if (c >= 0 && c < E && u <= rep_thr[c]) {
+            r = c;
+            break;
+          }
+        if (r < 0) fl |= MOE_FLAG_REPLICA;
+      } else {
+        fl |= MOE_FLAG_ID_RANGE;
+      }
+      map.out[i] = r;
+      e[s] = r;  // ranked as a physical replica; -1 drops the pair
+    }
+  }
 
   const unsigned long long below_me = (1ull << lane) - 1ull;
   int lr[R];
@@ -130,7 +177,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     const int i = wbase + s * kWave + lane;
     const bool in = i < end;
     const bool ok = in && e[s] >= 0 && e[s] < E;
-    if (in && !ok) fl |= MOE_FLAG_ID_RANGE;
+    if (in && !ok && !mapped) fl |= MOE_FLAG_ID_RANGE;
     if (ok) atomicOr(&mask[wave][e[s]], 1ull << lane);
     __builtin_amdgcn_wave_barrier();
     unsigned long long m = 0;
@@ -261,9 +308,10 @@ namespace {
 template <int R>
 void launch_rank(const LayoutPlan& plan, const int32_t* ids, int32_t k, int32_t E, int32_t align,
                  int32_t* expand_idx, int32_t* hist, int32_t* bflags, int32_t* counts,
-                 int32_t* send, int32_t* status, hipStream_t stream) {
+                 int32_t* send, int32_t* status, const ReplicaMap& map, hipStream_t stream) {
   layout_rank_kernel<R><<<plan.blocks, kLayoutThreads, 0, stream>>>(
-      ids, (int32_t)plan.n_pairs, k, E, align, expand_idx, hist, bflags, counts, send, status);
+      ids, (int32_t)plan.n_pairs, k, E, align, expand_idx, hist, bflags, counts, send, status,
+      map);
 }
 
 }  // namespace
@@ -271,7 +319,7 @@ void launch_rank(const LayoutPlan& plan, const int32_t* ids, int32_t k, int32_t 
 hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int32_t align,
                          const LayoutPlan& plan, int32_t* counts, int32_t* send,
                          int32_t* expand_idx, int32_t* status, void* workspace,
-                         hipStream_t stream) {
+                         const ReplicaMap& map, hipStream_t stream) {
   int32_t* hist = nullptr;
   int32_t* bflags = nullptr;
   if (plan.blocks > 1) {
@@ -282,21 +330,23 @@ hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int
   }
   switch (plan.rounds) {
     case 1: launch_rank<1>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, stream); break;
+                           send, status, map, stream); break;
     case 2: launch_rank<2>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, stream); break;
+                           send, status, map, stream); break;
     case 4: launch_rank<4>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, stream); break;
+                           send, status, map, stream); break;
     case 8: launch_rank<8>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, stream); break;
+                           send, status, map, stream); break;
     default: launch_rank<16>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                             send, status, stream); break;
+                             send, status, map, stream); break;
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.blocks <= 1) return err;
+  // The finalize pass looks pairs up by the id they were ranked under.
+  const int32_t* ranked_ids = map.offsets != nullptr ? map.out : ids;
   layout_finalize_kernel<<<plan.blocks, kLayoutThreads, 0, stream>>>(
-      ids, (int32_t)plan.n_pairs, num_experts, align, (int32_t)plan.pairs_per_block, plan.blocks,
-      hist, bflags, expand_idx, counts, send, status);
+      ranked_ids, (int32_t)plan.n_pairs, num_experts, align, (int32_t)plan.pairs_per_block,
+      plan.blocks, hist, bflags, expand_idx, counts, send, status);
   return hipGetLastError();
 }
 

@@ -150,13 +150,23 @@ constexpr int kLayoutThreads = kLayoutWaves * kWave;   // 512 pairs per round
 constexpr int kLayoutSingleMaxRounds = MOE_LAYOUT_SINGLE_ROUNDS;
 constexpr int kLayoutMultiRounds = MOE_LAYOUT_MULTI_ROUNDS;
 
+// Optional logical-expert -> physical-replica choice fused into the ranking
+// pass (offsets == nullptr: ids are ranked as given).
+struct ReplicaMap {
+  const int32_t* offsets = nullptr;      // [n_logical + 1] replica ranges
+  const uint32_t* thresholds = nullptr;  // [replicas] cumulative choice thresholds
+  int32_t n_logical = 0;
+  uint64_t seed = 0;
+  int32_t* out = nullptr;                // [n_pairs] chosen replica, -1 if none
+};
+
 LayoutPlan plan_layout(int32_t bs, int32_t k);
 size_t layout_workspace_bytes(const LayoutPlan& p, int32_t num_experts);
 
 hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int32_t align,
                          const LayoutPlan& plan, int32_t* counts, int32_t* send,
                          int32_t* expand_idx, int32_t* status, void* workspace,
-                         hipStream_t stream);
+                         const ReplicaMap& map, hipStream_t stream);
 
 // ---- dispatch / combine -----------------------------------------------------
 hipError_t launch_dispatch_bf16(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,

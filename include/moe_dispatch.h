@@ -61,7 +61,8 @@ enum moe_dtype {
 enum moe_flag {
     MOE_FLAG_ID_RANGE = 1,     /* some expert_ids value lies outside [0, num_experts) */
     MOE_FLAG_DUP_ID = 2,       /* some row of expert_ids repeats an expert */
-    MOE_FLAG_GUARD = 4         /* some slot fell outside [0, capacity_rows): pair skipped */
+    MOE_FLAG_GUARD = 4,        /* some slot fell outside [0, capacity_rows): pair skipped */
+    MOE_FLAG_REPLICA = 8       /* a replica table gave an expert no replica for some draw */
 };
 
 /* Version of this interface (incremented on any signature change). */
@@ -124,6 +125,44 @@ int moe_dispatch_layout(const int32_t* expert_ids, int32_t bs, int32_t k, int32_
                         int32_t align, int32_t* expert_counts, int32_t* ep_send_counts,
                         int32_t* expand_idx, int32_t* status, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * Replica-aware layout: the in-graph probabilistic dispatch with count
+ * gathering of the TEMPO summary (section 2, system integration), where hot
+ * experts have several physical replicas and each (token, k) pair is sent to
+ * one of them.  Replicas of logical expert e are the physical ids
+ * [replica_offsets[e], replica_offsets[e+1]), contiguous and disjoint.  Pair
+ * i = t*k + j draws u = the upper 32 bits of draw i of the SplitMix64 stream
+ * seeded with `seed` (Steele, Lea and Flood, OOPSLA 2014: the state
+ * seed + (i+1)*0x9E3779B97F4A7C15 through the variant-13 finaliser), and
+ * goes to the first replica r of its expert with u <= replica_thresholds[r]
+ * (thresholds are cumulative within an expert; the last should be
+ * 0xFFFFFFFF).  Then the layout of moe_dispatch_layout runs over the
+ * num_replicas physical replicas: replica_counts[r] is the token count N_r
+ * gathered per replica, ep_send_counts its 128-padded exclusive prefix (so
+ * replica r spans ceil(N_r/128) M-tiles), expand_idx the stable rank.
+ * Dispatch and combine then take replica_ids as their expert_ids with
+ * num_experts = num_replicas.
+ *
+ *  expert_ids          in  int32 [bs, k] logical experts in [0, num_experts).
+ *  replica_offsets     in  int32 [num_experts + 1], non-decreasing, last =
+ *                          num_replicas (device memory).
+ *  replica_thresholds  in  uint32 [num_replicas] (device memory).
+ *  num_replicas        in  1 <= num_replicas <= 512, k <= num_replicas.
+ *  replica_ids         out int32 [bs, k]: chosen replica, -1 if the logical id
+ *                          is out of range (MOE_FLAG_ID_RANGE) or the table
+ *                          gives none (MOE_FLAG_REPLICA); such pairs are
+ *                          dropped like out-of-range ids.
+ *  workspace           as for moe_dispatch_layout, sized with num_replicas.
+ * Other arguments as for moe_dispatch_layout.  Deterministic for a fixed seed.
+ */
+int moe_dispatch_layout_replicated(const int32_t* expert_ids, int32_t bs, int32_t k,
+                                   int32_t num_experts, const int32_t* replica_offsets,
+                                   const uint32_t* replica_thresholds, int32_t num_replicas,
+                                   uint64_t seed, int32_t align, int32_t* replica_ids,
+                                   int32_t* replica_counts, int32_t* ep_send_counts,
+                                   int32_t* expand_idx, int32_t* status, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /*
  * Dispatch: scatter token rows into the expert-contiguous buffer.

@@ -500,3 +500,81 @@ def test_fp8_round_trip_on_gpu():
     rc, rq, _ = oracle.dispatch_fp8(x_bits[sample], sub_ids, sub_r, s, w.experts, cap)
     ref, _ = oracle.combine_fp8(rc, rq, sub_ids, sub_r, s, sc[sample], None, w.experts)
     np.testing.assert_array_equal(host_bits(out[torch.from_numpy(sample).to(DEV)]), ref)
+
+
+# ------------------------------------------------------------------ replica-aware layout
+
+def random_replica_table(rng, e, max_rep):
+    reps = rng.integers(1, max_rep + 1, e)
+    off = np.concatenate([[0], np.cumsum(reps)]).astype(np.int32)
+    thr = np.empty(off[-1], np.uint32)
+    for x in range(e):
+        w = rng.random(reps[x]) + 0.05
+        c = np.cumsum(w / w.sum())
+        t = np.minimum(np.floor(c * 4294967296.0), 4294967295).astype(np.uint64)
+        t[-1] = 4294967295
+        thr[off[x]:off[x + 1]] = t.astype(np.uint32)
+    return off, thr
+
+
+def assert_replicated_equal(ids, e, off, thr, seed, align):
+    moe = moe_mod()
+    rep, c, s, r, f = oracle.layout_replicated(ids, e, off, thr, seed, align)
+    grep, lay = moe.moe_dispatch_layout_replicated(
+        dev(ids), e, dev(off), dev(thr.view(np.int32)), seed, align)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(grep.cpu().numpy(), rep)
+    np.testing.assert_array_equal(lay.expert_counts.cpu().numpy(), c)
+    np.testing.assert_array_equal(lay.ep_send_counts.cpu().numpy(), s)
+    np.testing.assert_array_equal(lay.expand_idx.cpu().numpy(), r)
+    assert int(lay.status.cpu()[0]) == f
+    return rep, s, r, lay, grep
+
+
+@pytest.mark.parametrize("bs,e,k,max_rep,seed", [(1, 1, 1, 1, 0), (64, 8, 2, 3, 5),
+                                                 (700, 64, 8, 4, 11), (4096, 256, 8, 2, 2 ** 40 + 3),
+                                                 (5000, 100, 6, 5, 77)])
+def test_replicated_layout_matches_oracle(bs, e, k, max_rep, seed):
+    rng = np.random.default_rng(bs + e)
+    off, thr = random_replica_table(rng, e, max_rep)
+    if off[-1] > 512:
+        pytest.skip("more than 512 replicas")
+    ids = random_ids(rng, bs, e, k)
+    for align in (1, 128):
+        assert_replicated_equal(ids, e, off, thr, seed, align)
+
+
+def test_replicated_layout_flags():
+    rng = np.random.default_rng(3)
+    e, k, bs = 16, 4, 3000
+    off, thr = random_replica_table(rng, e, 3)
+    ids = random_ids(rng, bs, e, k)
+    ids[::11, 0] = e + 3                     # out-of-range logical ids
+    ids[::13, 2] = ids[::13, 1]              # repeated experts
+    thr = thr.copy()
+    thr[off[5]:off[6]] = 0                   # expert 5 can only map when u == 0
+    rep, s, r, lay, grep = assert_replicated_equal(ids, e, off, thr, 9, 128)
+    f = int(lay.status.cpu()[0])
+    assert f & oracle.FLAG_ID_RANGE and f & oracle.FLAG_DUP_ID and f & oracle.FLAG_REPLICA
+
+
+def test_replicated_pipeline_round_trip():
+    """Skewed routing with the 16 hottest experts split into 4 replicas:
+    dispatch and combine over the replicas with identity experts return x."""
+    moe = moe_mod()
+    w = workloads.WORKLOADS["skewed"]
+    ids = workloads.routing(w.bs, w.experts, w.topk, w.routing, w.alpha, w.seed)
+    hot = workloads.popularity(w.experts, w.routing, w.seed)[:16]
+    off, thr = workloads.replica_plan(w.experts, hot, 4)
+    p = int(off[-1])
+    rep, s, r, lay, grep = assert_replicated_equal(ids, w.experts, off, thr, 1234, 128)
+    c_plain = oracle.layout(ids, w.experts, 128)[0]
+    # counts gathered per replica add back up to the logical counts
+    c_rep = lay.expert_counts.cpu().numpy()
+    np.testing.assert_array_equal(np.add.reduceat(c_rep, off[:-1]), c_plain)
+    x = workloads.bf16_rows(w.bs, w.hidden, w.seed).to(DEV)
+    ex = moe.moe_dispatch(x, grep, lay.expand_idx, lay.ep_send_counts, p)
+    out = moe.moe_combine(ex, grep, lay.expand_idx, lay.ep_send_counts,
+                          dev(workloads.scales(w.bs, w.topk, w.seed)), None, p)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), x.view(torch.int16))

@@ -135,6 +135,31 @@ def e4m3_rows(rows: int, cols: int, seed: int, stream: str = "y"):
     return codes, scales
 
 
+def popularity(experts: int, kind: str = "zipf", seed: int = 0) -> np.ndarray:
+    """Experts from most to least popular under the workload's Zipf draw (the
+    same seeded permutation ``routing`` uses); uniform routing has no order."""
+    if kind != "zipf":
+        return np.arange(experts)
+    rng = np.random.default_rng(seed_streams(seed)["routing"])
+    return rng.permutation(experts)
+
+
+def replica_plan(experts: int, hot: np.ndarray, replicas_per_hot: int):
+    """A synthetic replica table: each expert in ``hot`` gets
+    ``replicas_per_hot`` physical replicas chosen with equal probability, every
+    other expert one.  Returns (offsets int32 [E+1], thresholds uint32 [P]) in
+    the cumulative-threshold form the replica-aware layout takes."""
+    reps = np.ones(experts, np.int64)
+    reps[np.asarray(hot, np.int64)] = replicas_per_hot
+    offsets = np.concatenate([[0], np.cumsum(reps)]).astype(np.int32)
+    thresholds = np.empty(int(offsets[-1]), np.uint32)
+    for e in range(experts):
+        g = int(reps[e])
+        cuts = [((j + 1) * (1 << 32)) // g - 1 for j in range(g)]
+        thresholds[offsets[e]:offsets[e + 1]] = np.array(cuts, np.uint64).astype(np.uint32)
+    return offsets, thresholds
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """uint16 bit patterns of a CPU bfloat16 tensor (a view, no copy)."""
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
