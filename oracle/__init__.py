@@ -20,6 +20,8 @@ expert_scales / shared_expert_x; TEMPO summary section 1 for the 128-row tile):
   unweighted shared row, rounded to bf16 (nearest-even).
 * ``combine_fp8`` -- the same sum over e4m3 expert rows, each term dequantised
   as ``e4m3_value * scale`` (one binary32 multiply) first.
+* ``layout_ep``   -- the layout plus per-destination-rank send offsets for
+  E/ws contiguous experts per rank (combine page, A3 ep_send_counts shape).
 * ``layout_replicated`` -- each pair picks a physical replica of its expert
   by a SplitMix64 draw against cumulative thresholds (TEMPO summary, section
   2, system integration), then the layout runs over the replicas.
@@ -100,6 +102,7 @@ def _load():
                                           P, P]),
         "oracle_combine_fp8": (ctypes.c_int, [P, i64, i64, P, P, P, P, P, P, i64, i32, i32,
                                               i32, i32, P, P]),
+        "oracle_layout_ep": (ctypes.c_int, [P, i32, i32, i32, i32, i32, P, P, P, P, P]),
         "oracle_splitmix64": (ctypes.c_uint64, [ctypes.c_uint64, ctypes.c_uint64]),
         "oracle_layout_replicated": (ctypes.c_int, [P, i32, i32, i32, P, P, i32, ctypes.c_uint64,
                                                     i32, P, P, P, P, P]),
@@ -316,3 +319,19 @@ def layout_replicated(expert_ids: np.ndarray, num_experts: int, replica_offsets:
     if rc != OK:
         raise OracleArgError(rc)
     return rep, counts, send, idx, int(flags[0])
+
+
+def layout_ep(expert_ids: np.ndarray, num_experts: int, ep_world_size: int, align: int = 128):
+    """Returns ``(expert_counts, ep_send_counts, rank_offsets[ws+1], expand_idx, flags)``."""
+    ids = _i32(expert_ids)
+    bs, k = ids.shape
+    counts = np.zeros(num_experts, np.int32)
+    send = np.zeros(num_experts + 1, np.int32)
+    ranks = np.zeros(max(ep_world_size, 0) + 1, np.int32)
+    idx = np.zeros(bs * k, np.int32)
+    flags = np.zeros(1, np.int32)
+    rc = _load().oracle_layout_ep(_ptr(ids), bs, k, num_experts, ep_world_size, align,
+                                  _ptr(counts), _ptr(send), _ptr(ranks), _ptr(idx), _ptr(flags))
+    if rc != OK:
+        raise OracleArgError(rc)
+    return counts, send, ranks, idx, int(flags[0])

@@ -416,6 +416,32 @@ int oracle_combine_fp8(const uint8_t* y, int64_t y_stride, int64_t capacity_rows
 }
 
 /* ------------------------------------------------------------------------ */
+/* Rank-partitioned layout (combine page, ep_send_counts for the A3 series:  */
+/* ep_world_size * local_expert_num entries; moe_expert_num divisible by the  */
+/* number of expert ranks).                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Expert e lives on rank e / L with L = E / ep_world_size experts per rank,
+ * so the expert-contiguous layout is already rank-major.  The rows bound for
+ * rank r are [rank_offsets[r], rank_offsets[r+1]) with
+ * rank_offsets[r] = ep_send_counts[r*L] (and rank_offsets[ws] = the total):
+ * the per-destination send offsets of an all-to-all(v).  E must be a
+ * multiple of ep_world_size. */
+int oracle_layout_ep(const int32_t* expert_ids, int32_t bs, int32_t k, int32_t num_experts,
+                     int32_t ep_world_size, int32_t align, int32_t* expert_counts,
+                     int32_t* ep_send_counts, int32_t* rank_offsets, int32_t* expand_idx,
+                     int32_t* flags) {
+    if (ep_world_size < 1 || ep_world_size > num_experts || num_experts % ep_world_size != 0)
+        return ORC_ERR_INVALID_ARG;
+    int rc = oracle_layout(expert_ids, bs, k, num_experts, align, expert_counts,
+                           ep_send_counts, expand_idx, flags);
+    if (rc != ORC_OK) return rc;
+    int32_t per_rank = num_experts / ep_world_size;
+    for (int32_t r = 0; r <= ep_world_size; ++r) rank_offsets[r] = ep_send_counts[r * per_rank];
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Replica-aware dispatch (TEMPO summary, section 2, system integration: one  */
 /* in-graph kernel does the probabilistic replica choice and the counting).  */
 /* ------------------------------------------------------------------------ */
