@@ -16,6 +16,8 @@ Entry points (same names as the C ABI):
   expert_scales, shared_expert_x)`` -> ``x_out``
 * ``moe_combine_fp8(expand_x_codes, quant_scales, ...)`` -> ``x_out`` (expert
   rows in the e4m3 + per-128-channel scale format, dequantised in the gather)
+* ``moe_dispatch_layout_ep(expert_ids, num_experts, ep_world_size)`` ->
+  ``(Layout, rank_offsets [ws+1])``
 * ``moe_dispatch_layout_replicated(expert_ids, num_experts, replica_offsets,
   replica_thresholds, seed)`` -> ``(replica_ids, Layout over replicas)``
 * ``moe_dispatch_capacity`` / ``moe_dispatch_layout_workspace_size``
@@ -32,7 +34,8 @@ import torch
 __all__ = [
     "MoeError", "Layout", "library_path", "load_library",
     "moe_dispatch_capacity", "moe_dispatch_layout_workspace_size",
-    "moe_dispatch_layout", "moe_dispatch_layout_replicated", "moe_dispatch", "moe_combine",
+    "moe_dispatch_layout", "moe_dispatch_layout_ep", "moe_dispatch_layout_replicated",
+    "moe_dispatch", "moe_combine",
     "moe_combine_fp8",
     "MOE_BF16", "MOE_FP8_E4M3", "MOE_FLAG_ID_RANGE", "MOE_FLAG_DUP_ID", "MOE_FLAG_GUARD",
 ]
@@ -80,6 +83,8 @@ def load_library() -> ctypes.CDLL:
                                        P, P]),
         "moe_combine_fp8": (ctypes.c_int, [P, i64, i64, P, P, P, P, P, P, i64, i32, i32, i32,
                                            i32, P, P, P]),
+        "moe_dispatch_layout_ep": (ctypes.c_int, [P, i32, i32, i32, i32, i32, P, P, P, P, P, P,
+                                                  sz, P]),
         "moe_dispatch_layout_replicated": (ctypes.c_int, [P, i32, i32, i32, P, P, i32,
                                                           ctypes.c_uint64, i32, P, P, P, P, P, P,
                                                           sz, P]),
@@ -295,3 +300,32 @@ def moe_dispatch_layout_replicated(expert_ids: torch.Tensor, num_experts: int,
         _stream(expert_ids))
     _check(rc)
     return replica_ids, out
+
+
+def moe_dispatch_layout_ep(expert_ids: torch.Tensor, num_experts: int, ep_world_size: int,
+                           align: int = 128, *, out: Optional[Layout] = None,
+                           rank_offsets: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None):
+    """The layout plus per-destination-rank send offsets (experts split evenly
+    and contiguously over ``ep_world_size`` ranks).  Returns
+    ``(Layout, rank_offsets int32 [ws+1])``."""
+    _need(expert_ids, torch.int32, "expert_ids")
+    bs, k = expert_ids.shape
+    dev = expert_ids.device
+    if out is None:
+        out = Layout(torch.empty(num_experts, dtype=torch.int32, device=dev),
+                     torch.empty(num_experts + 1, dtype=torch.int32, device=dev),
+                     torch.empty(bs * k, dtype=torch.int32, device=dev),
+                     torch.empty(1, dtype=torch.int32, device=dev))
+    if rank_offsets is None:
+        rank_offsets = torch.empty(max(ep_world_size, 0) + 1, dtype=torch.int32, device=dev)
+    ws_bytes = moe_dispatch_layout_workspace_size(bs, k, num_experts)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    rc = load_library().moe_dispatch_layout_ep(
+        _ptr(expert_ids), bs, k, num_experts, ep_world_size, align, _ptr(out.expert_counts),
+        _ptr(out.ep_send_counts), _ptr(rank_offsets), _ptr(out.expand_idx), _ptr(out.status),
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(expert_ids))
+    _check(rc)
+    return out, rank_offsets

@@ -92,7 +92,33 @@ int moe_dispatch_layout(const int32_t* expert_ids, int32_t bs, int32_t k, int32_
     return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_layout(expert_ids, k, num_experts, align, plan, expert_counts,
                                        ep_send_counts, expand_idx, status, workspace,
-                                       moe::ReplicaMap{}, static_cast<hipStream_t>(stream)));
+                                       moe::ReplicaMap{}, moe::RankSplit{},
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int moe_dispatch_layout_ep(const int32_t* expert_ids, int32_t bs, int32_t k, int32_t num_experts,
+                           int32_t ep_world_size, int32_t align, int32_t* expert_counts,
+                           int32_t* ep_send_counts, int32_t* rank_offsets, int32_t* expand_idx,
+                           int32_t* status, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (!layout_args_ok(bs, k, num_experts, align)) return MOE_ERR_INVALID_ARG;
+  if (ep_world_size < 1 || ep_world_size > num_experts || num_experts % ep_world_size != 0)
+    return MOE_ERR_INVALID_ARG;
+  if (expert_counts == nullptr || ep_send_counts == nullptr || rank_offsets == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (bs > 0 && (expert_ids == nullptr || expand_idx == nullptr)) return MOE_ERR_INVALID_ARG;
+  const moe::LayoutPlan plan = moe::plan_layout(bs, k);
+  const size_t need = moe::layout_workspace_bytes(plan, num_experts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return MOE_ERR_WORKSPACE;
+  moe::RankSplit ranks;
+  ranks.offsets = rank_offsets;
+  ranks.per_rank = num_experts / ep_world_size;
+  ranks.ranks = ep_world_size;
+  return hip_status(moe::launch_layout(expert_ids, k, num_experts, align, plan, expert_counts,
+                                       ep_send_counts, expand_idx, status, workspace,
+                                       moe::ReplicaMap{}, ranks,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 int moe_dispatch_layout_replicated(const int32_t* expert_ids, int32_t bs, int32_t k,
@@ -121,7 +147,7 @@ int moe_dispatch_layout_replicated(const int32_t* expert_ids, int32_t bs, int32_
   map.out = replica_ids;
   return hip_status(moe::launch_layout(expert_ids, k, num_replicas, align, plan, replica_counts,
                                        ep_send_counts, expand_idx, status, workspace, map,
-                                       static_cast<hipStream_t>(stream)));
+                                       moe::RankSplit{}, static_cast<hipStream_t>(stream)));
 }
 
 int moe_dispatch(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,

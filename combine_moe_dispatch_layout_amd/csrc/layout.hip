@@ -55,10 +55,11 @@ __device__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
   return before + incl - v;
 }
 
-// Thread e holds c_e (0 for e >= E).  Writes counts[e], send[e] and send[E].
+// Thread e holds c_e (0 for e >= E).  Writes counts[e], send[e] and send[E];
+// with a rank split also the per-destination-rank offsets send[r * per_rank].
 __device__ void write_counts_and_offsets(int c, int32_t E, int32_t align, int* wave_tot,
                                          int32_t* __restrict__ counts,
-                                         int32_t* __restrict__ send) {
+                                         int32_t* __restrict__ send, const RankSplit& ranks) {
   const int e = threadIdx.x;
   const int padded = (c + align - 1) & ~(align - 1);
   int total;
@@ -66,8 +67,12 @@ __device__ void write_counts_and_offsets(int c, int32_t E, int32_t align, int* w
   if (e < E) {
     counts[e] = c;
     send[e] = excl;
+    if (ranks.offsets != nullptr && e % ranks.per_rank == 0) ranks.offsets[e / ranks.per_rank] = excl;
   }
-  if (e == 0) send[E] = total;
+  if (e == 0) {
+    send[E] = total;
+    if (ranks.offsets != nullptr) ranks.offsets[ranks.ranks] = total;
+  }
 }
 
 // Flags an expert (an id in [0, E)) repeated within one of the tokens whose
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     const int32_t* __restrict__ ids, int32_t n_pairs, int32_t k, int32_t E, int32_t align,
     int32_t* __restrict__ expand_idx, int32_t* __restrict__ block_hist,
     int32_t* __restrict__ block_flags, int32_t* __restrict__ counts, int32_t* __restrict__ send,
-    int32_t* __restrict__ status, ReplicaMap map) {
+    int32_t* __restrict__ status, ReplicaMap map, RankSplit ranks) {
   __shared__ unsigned long long mask[kLayoutWaves][kMaxExperts];  // 32 KB
   __shared__ int wave_run[kLayoutWaves][kMaxExperts];             // 16 KB
   __shared__ int rep_off[kMaxExperts + 1];
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
 
   if (block_hist == nullptr) {
     // The whole batch was this workgroup: finish the layout here.
-    write_counts_and_offsets(tot, E, align, wave_tot, counts, send);
+    write_counts_and_offsets(tot, E, align, wave_tot, counts, send, ranks);
     if (tid == 0 && status) *status = flags_lds;
   } else {
     if (tid < E) block_hist[blockIdx.x * E + tid] = tot;
@@ -230,7 +235,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
     const int32_t* __restrict__ ids, int32_t n_pairs, int32_t E, int32_t align,
     int32_t pairs_per_block, int32_t nblocks, const int32_t* __restrict__ block_hist,
     const int32_t* __restrict__ block_flags, int32_t* __restrict__ expand_idx,
-    int32_t* __restrict__ counts, int32_t* __restrict__ send, int32_t* __restrict__ status) {
+    int32_t* __restrict__ counts, int32_t* __restrict__ send, int32_t* __restrict__ status,
+    RankSplit ranks) {
   __shared__ int base[kMaxExperts];
   __shared__ int wave_tot[kLayoutWaves];
   const int b = blockIdx.x;
@@ -250,7 +256,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
     if (last) own = s + block_hist[b * E + tid];
   }
   if (last) {  // workgroup-uniform
-    write_counts_and_offsets(own, E, align, wave_tot, counts, send);
+    write_counts_and_offsets(own, E, align, wave_tot, counts, send, ranks);
     int f = 0;
     for (int bb = tid; bb < nblocks; bb += kLayoutThreads) f |= block_flags[bb];
     if (f) atomicOr(&flags_lds, f);
@@ -308,10 +314,11 @@ namespace {
 template <int R>
 void launch_rank(const LayoutPlan& plan, const int32_t* ids, int32_t k, int32_t E, int32_t align,
                  int32_t* expand_idx, int32_t* hist, int32_t* bflags, int32_t* counts,
-                 int32_t* send, int32_t* status, const ReplicaMap& map, hipStream_t stream) {
+                 int32_t* send, int32_t* status, const ReplicaMap& map, const RankSplit& ranks,
+                 hipStream_t stream) {
   layout_rank_kernel<R><<<plan.blocks, kLayoutThreads, 0, stream>>>(
       ids, (int32_t)plan.n_pairs, k, E, align, expand_idx, hist, bflags, counts, send, status,
-      map);
+      map, ranks);
 }
 
 }  // namespace
@@ -319,7 +326,7 @@ void launch_rank(const LayoutPlan& plan, const int32_t* ids, int32_t k, int32_t 
 hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int32_t align,
                          const LayoutPlan& plan, int32_t* counts, int32_t* send,
                          int32_t* expand_idx, int32_t* status, void* workspace,
-                         const ReplicaMap& map, hipStream_t stream) {
+                         const ReplicaMap& map, const RankSplit& ranks, hipStream_t stream) {
   int32_t* hist = nullptr;
   int32_t* bflags = nullptr;
   if (plan.blocks > 1) {
@@ -330,15 +337,15 @@ hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int
   }
   switch (plan.rounds) {
     case 1: launch_rank<1>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, map, stream); break;
+                           send, status, map, ranks, stream); break;
     case 2: launch_rank<2>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, map, stream); break;
+                           send, status, map, ranks, stream); break;
     case 4: launch_rank<4>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, map, stream); break;
+                           send, status, map, ranks, stream); break;
     case 8: launch_rank<8>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, map, stream); break;
+                           send, status, map, ranks, stream); break;
     default: launch_rank<16>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                             send, status, map, stream); break;
+                             send, status, map, ranks, stream); break;
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.blocks <= 1) return err;
@@ -346,7 +353,7 @@ hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int
   const int32_t* ranked_ids = map.offsets != nullptr ? map.out : ids;
   layout_finalize_kernel<<<plan.blocks, kLayoutThreads, 0, stream>>>(
       ranked_ids, (int32_t)plan.n_pairs, num_experts, align, (int32_t)plan.pairs_per_block,
-      plan.blocks, hist, bflags, expand_idx, counts, send, status);
+      plan.blocks, hist, bflags, expand_idx, counts, send, status, ranks);
   return hipGetLastError();
 }
 

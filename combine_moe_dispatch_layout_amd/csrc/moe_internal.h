@@ -160,13 +160,21 @@ struct ReplicaMap {
   int32_t* out = nullptr;                // [n_pairs] chosen replica, -1 if none
 };
 
+// Optional per-destination-rank offsets written with the padded scan:
+// offsets[r] = send[r * per_rank] for r < ranks, offsets[ranks] = total.
+struct RankSplit {
+  int32_t* offsets = nullptr;
+  int32_t per_rank = 1;
+  int32_t ranks = 0;
+};
+
 LayoutPlan plan_layout(int32_t bs, int32_t k);
 size_t layout_workspace_bytes(const LayoutPlan& p, int32_t num_experts);
 
 hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int32_t align,
                          const LayoutPlan& plan, int32_t* counts, int32_t* send,
                          int32_t* expand_idx, int32_t* status, void* workspace,
-                         const ReplicaMap& map, hipStream_t stream);
+                         const ReplicaMap& map, const RankSplit& ranks, hipStream_t stream);
 
 // ---- dispatch / combine -----------------------------------------------------
 hipError_t launch_dispatch_bf16(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,

@@ -127,6 +127,27 @@ int moe_dispatch_layout(const int32_t* expert_ids, int32_t bs, int32_t k, int32_
                         size_t workspace_bytes, void* stream);
 
 /*
+ * Rank-partitioned layout: moe_dispatch_layout plus the per-destination-rank
+ * send offsets an expert-parallel all-to-all(v) needs.  The combine page's
+ * A3-series ep_send_counts has ep_world_size * local_expert_num entries and
+ * its expert count must divide evenly over the expert ranks: expert e lives
+ * on rank e / L with L = num_experts / ep_world_size, so the expert-major
+ * layout is already rank-major and rank r's rows are
+ *   [rank_offsets[r], rank_offsets[r+1]),  rank_offsets[r] = ep_send_counts[r*L],
+ * rank_offsets[ep_world_size] = the padded total.  With align = 1 the send
+ * buffer carries no padding rows.
+ *
+ *  ep_world_size  in  1 <= ep_world_size <= num_experts, dividing num_experts.
+ *  rank_offsets   out int32 [ep_world_size + 1].
+ * Other arguments and outputs as for moe_dispatch_layout.
+ */
+int moe_dispatch_layout_ep(const int32_t* expert_ids, int32_t bs, int32_t k, int32_t num_experts,
+                           int32_t ep_world_size, int32_t align, int32_t* expert_counts,
+                           int32_t* ep_send_counts, int32_t* rank_offsets, int32_t* expand_idx,
+                           int32_t* status, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * Replica-aware layout: the in-graph probabilistic dispatch with count
  * gathering of the TEMPO summary (section 2, system integration), where hot
  * experts have several physical replicas and each (token, k) pair is sent to

@@ -167,3 +167,21 @@ def test_combine_fp8_rules(lib):
     assert call(k=17) == 1
     assert lib.moe_combine_fp8(FAKE, 128, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 0, 128, 2,
                                8, FAKE, None, None) == 0   # empty batch
+
+
+@pytest.mark.parametrize("e,ws", [(16, 3), (16, 0), (8, 16), (16, -2)])
+def test_layout_ep_rejects_like_the_oracle(lib, e, ws):
+    with pytest.raises(oracle.OracleArgError):
+        oracle.layout_ep(np.zeros((2, 1), np.int32), e, ws, 128)
+    assert lib.moe_dispatch_layout_ep(FAKE, 2, 1, e, ws, 128, FAKE, FAKE, FAKE, FAKE, None, None,
+                                      0, None) == 1
+
+
+def test_layout_replicated_rules(lib):
+    # replicas must admit k distinct choices; tables are required
+    assert lib.moe_dispatch_layout_replicated(FAKE, 4, 2, 8, FAKE, FAKE, 1, 0, 128, FAKE, FAKE,
+                                              FAKE, FAKE, None, None, 0, None) == 1
+    assert lib.moe_dispatch_layout_replicated(FAKE, 4, 2, 8, None, FAKE, 8, 0, 128, FAKE, FAKE,
+                                              FAKE, FAKE, None, None, 0, None) == 1
+    assert lib.moe_dispatch_layout_replicated(FAKE, 4, 2, 8, FAKE, FAKE, 513, 0, 128, FAKE,
+                                              FAKE, FAKE, FAKE, None, None, 0, None) == 1

@@ -578,3 +578,22 @@ def test_replicated_pipeline_round_trip():
                           dev(workloads.scales(w.bs, w.topk, w.seed)), None, p)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), x.view(torch.int16))
+
+
+# ------------------------------------------------------------------ rank-partitioned layout
+
+@pytest.mark.parametrize("bs,e,k,ws", [(1, 1, 1, 1), (300, 64, 8, 8), (4096, 256, 8, 8),
+                                       (5000, 512, 8, 64), (777, 96, 6, 12)])
+def test_layout_ep_matches_oracle(bs, e, k, ws):
+    moe = moe_mod()
+    rng = np.random.default_rng(bs + ws)
+    ids = random_ids(rng, bs, e, k)
+    for align in (1, 128):
+        c, s, ranks, r, f = oracle.layout_ep(ids, e, ws, align)
+        lay, granks = moe.moe_dispatch_layout_ep(dev(ids), e, ws, align)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(lay.expert_counts.cpu().numpy(), c)
+        np.testing.assert_array_equal(lay.ep_send_counts.cpu().numpy(), s)
+        np.testing.assert_array_equal(lay.expand_idx.cpu().numpy(), r)
+        np.testing.assert_array_equal(granks.cpu().numpy(), ranks)
+        assert int(lay.status.cpu()[0]) == f
