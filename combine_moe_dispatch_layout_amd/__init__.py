@@ -20,6 +20,8 @@ Entry points (same names as the C ABI):
   ``(Layout, rank_offsets [ws+1])``
 * ``moe_dispatch_layout_replicated(expert_ids, num_experts, replica_offsets,
   replica_thresholds, seed)`` -> ``(replica_ids, Layout over replicas)``
+* ``moe_plan_compensation(expert_counts, ep_world_size, tile_cost,
+  activation_cost)`` -> dict (host-side 128-aligned chunk-migration plan)
 * ``moe_dispatch_capacity`` / ``moe_dispatch_layout_workspace_size``
 """
 
@@ -27,6 +29,8 @@ from __future__ import annotations
 
 import ctypes
 import os
+
+import numpy as np
 from typing import NamedTuple, Optional
 
 import torch
@@ -35,7 +39,7 @@ __all__ = [
     "MoeError", "Layout", "library_path", "load_library",
     "moe_dispatch_capacity", "moe_dispatch_layout_workspace_size",
     "moe_dispatch_layout", "moe_dispatch_layout_ep", "moe_dispatch_layout_replicated",
-    "moe_dispatch", "moe_combine",
+    "moe_dispatch", "moe_combine", "moe_plan_compensation",
     "moe_combine_fp8",
     "MOE_BF16", "MOE_FP8_E4M3", "MOE_FLAG_ID_RANGE", "MOE_FLAG_DUP_ID", "MOE_FLAG_GUARD",
 ]
@@ -83,6 +87,8 @@ def load_library() -> ctypes.CDLL:
                                        P, P]),
         "moe_combine_fp8": (ctypes.c_int, [P, i64, i64, P, P, P, P, P, P, i64, i32, i32, i32,
                                            i32, P, P, P]),
+        "moe_plan_compensation": (ctypes.c_int, [P, i32, i32, i64, i64, i64, i32, P, P, P, P, P,
+                                                 P]),
         "moe_dispatch_layout_ep": (ctypes.c_int, [P, i32, i32, i32, i32, i32, P, P, P, P, P, P,
                                                   sz, P]),
         "moe_dispatch_layout_replicated": (ctypes.c_int, [P, i32, i32, i32, P, P, i32,
@@ -329,3 +335,25 @@ def moe_dispatch_layout_ep(expert_ids: torch.Tensor, num_experts: int, ep_world_
         _stream(expert_ids))
     _check(rc)
     return out, rank_offsets
+
+
+def moe_plan_compensation(expert_counts, ep_world_size: int, tile_cost: int,
+                          activation_cost: int, min_gain: int = 0, max_moves: int = 1024) -> dict:
+    """Host-side 128-aligned compensation plan over per-expert token counts
+    (any int sequence, numpy array or CPU tensor).  Returns dict(moves=[(expert,
+    src, dst, rows)], loads=[...], before, after, ideal)."""
+    if isinstance(expert_counts, torch.Tensor):
+        expert_counts = expert_counts.detach().cpu().numpy()
+    counts = np.ascontiguousarray(expert_counts, dtype=np.int32)
+    moves = np.zeros((max(max_moves, 1), 4), dtype=np.int32)
+    n = ctypes.c_int32(0)
+    loads = np.zeros(max(ep_world_size, 1), dtype=np.int64)
+    before, after, ideal = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    rc = load_library().moe_plan_compensation(
+        counts.ctypes.data, counts.size, ep_world_size, tile_cost, activation_cost, min_gain,
+        max_moves, moves.ctypes.data, ctypes.byref(n), loads.ctypes.data, ctypes.byref(before),
+        ctypes.byref(after), ctypes.byref(ideal))
+    _check(rc)
+    return {"moves": [tuple(int(v) for v in row) for row in moves[:n.value]],
+            "loads": [int(v) for v in loads[:ep_world_size]], "before": before.value,
+            "after": after.value, "ideal": ideal.value}

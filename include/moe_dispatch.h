@@ -277,6 +277,43 @@ int moe_combine_fp8(const void* expand_x, int64_t expand_x_stride, int64_t capac
                     int64_t shared_stride, int32_t bs, int32_t hidden, int32_t k,
                     int32_t num_experts, void* x_out, int32_t* status, void* stream);
 
+/*
+ * Compensation planner (host code, host pointers; no GPU involved).  The
+ * DeepEP compensation PR (Python section) describes a water-filling
+ * chunk-migration planner with expert-affinity batching, a makespan guard, a
+ * cost-aware no-op and 128-aligned chunks; the TEMPO summary (section 2)
+ * prices an expert on a device as an activation floor plus a cost per
+ * 128-row M-tile.  With expert e homed on rank e / (E / ep_world_size), the
+ * load of a rank is the sum over the experts it computes of
+ *   activation_cost + tile_cost * ceil(rows / 128).
+ * The planner repeatedly moves whole 128-row chunks of one expert from the
+ * most to the least loaded rank (lowest index on ties): the move minimising
+ * the pair's new maximum, ties to an expert the receiver already computes,
+ * then the lower expert id, then fewer chunks; a move is admitted only if
+ * the receiver stays below the current makespan; it stops when the two loads
+ * differ by at most one tile, no move is admitted or max_moves are made, and
+ * returns no move at all if the makespan fell by less than min_gain.
+ *
+ *  expert_counts   in  int32 [num_experts] (host): tokens per expert, >= 0,
+ *                      e.g. the layout's expert_counts summed over ranks.
+ *  ep_world_size   in  >= 1, dividing num_experts (<= 2^20).
+ *  tile_cost, activation_cost, min_gain
+ *                  in  integer cost units (tile_cost > 0, others >= 0).
+ *  moves           out int32 [max_moves][4] (host): expert, source rank,
+ *                      destination rank, rows (a multiple of 128).
+ *  n_moves         out number of moves written.
+ *  rank_loads      out int64 [ep_world_size] (host): loads after the plan.
+ *  makespan_before, makespan_after, ideal
+ *                  out (nullable): largest load before and after, and the
+ *                      ideal bound ceil(sum of starting loads / ranks).
+ * Returns MOE_ERR_INVALID_ARG for bad arguments; never touches the GPU.
+ */
+int moe_plan_compensation(const int32_t* expert_counts, int32_t num_experts,
+                          int32_t ep_world_size, int64_t tile_cost, int64_t activation_cost,
+                          int64_t min_gain, int32_t max_moves, int32_t* moves, int32_t* n_moves,
+                          int64_t* rank_loads, int64_t* makespan_before, int64_t* makespan_after,
+                          int64_t* ideal);
+
 #ifdef __cplusplus
 }
 #endif
