@@ -31,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
-EVENT_EVERY = 4         # combine launches bracketed by events: every 4th step
+EVENT_EVERY = 10        # combine launches bracketed by events: every 10th step
 METRIC = "dispatch+combine achieved HBM GB/s and tokens/s, H=7168 E=256 K=8 bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_bf16_skewed_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_moe_dispatch_layout_amd", "csrc", f)
@@ -41,7 +41,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "combine_moe_dispatch_layout_amd", "csrc", 
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="skewed",
                    choices=["tiny", "decode", "skewed", "fp8", "large"])

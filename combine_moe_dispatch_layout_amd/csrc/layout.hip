@@ -245,15 +245,27 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
 
   __shared__ int flags_lds;
   if (tid == 0) flags_lds = 0;
+  // This workgroup's pairs (the same split as the ranking pass): their loads
+  // do not depend on the histograms, so they are issued first and are in
+  // flight while the column sums below are formed.
+  const int begin = b * pairs_per_block;
+  const int end = min(n_pairs, begin + pairs_per_block);
+  int r[kLayoutMultiRounds], e[kLayoutMultiRounds];
+#pragma unroll
+  for (int s = 0; s < kLayoutMultiRounds; ++s) {
+    const int i = begin + s * kLayoutThreads + tid;
+    r[s] = (i < end) ? expand_idx[i] : -1;
+    e[s] = (i < end) ? ids[i] : 0;
+  }
   // Column sums over the earlier workgroups' histograms; the loads of one
   // batch of rows are independent, so they are issued together.
   int own = 0;
   if (tid < E) {
-    int s = 0;
+    int sum = 0;
 #pragma unroll 8
-    for (int bb = 0; bb < b; ++bb) s += block_hist[bb * E + tid];
-    base[tid] = s;
-    if (last) own = s + block_hist[b * E + tid];
+    for (int bb = 0; bb < b; ++bb) sum += block_hist[bb * E + tid];
+    base[tid] = sum;
+    if (last) own = sum + block_hist[b * E + tid];
   }
   if (last) {  // workgroup-uniform
     write_counts_and_offsets(own, E, align, wave_tot, counts, send, ranks);
@@ -265,17 +277,6 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
   }
   __syncthreads();
 
-  // Every workgroup of this pass covers kLayoutMultiRounds * kLayoutThreads
-  // pairs; all of a thread's loads are issued before any of its stores.
-  const int begin = b * pairs_per_block;
-  const int end = min(n_pairs, begin + pairs_per_block);
-  int r[kLayoutMultiRounds], e[kLayoutMultiRounds];
-#pragma unroll
-  for (int s = 0; s < kLayoutMultiRounds; ++s) {
-    const int i = begin + s * kLayoutThreads + tid;
-    r[s] = (i < end) ? expand_idx[i] : -1;
-    e[s] = (i < end) ? ids[i] : 0;
-  }
 #pragma unroll
   for (int s = 0; s < kLayoutMultiRounds; ++s) {
     const int i = begin + s * kLayoutThreads + tid;
