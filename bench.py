@@ -7,13 +7,16 @@ expert-contiguous, 128-row-padded buffer) -> moe_combine (weighted gather-sum
 + shared row).  Inputs are seeded synthetic tensors already resident in HBM
 when the timed region starts.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload skewed]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload skewed] [--graph]
 
 `value` is algorithmic bytes per step (real rows only, never padding) divided
 by the measured step time, in GB/s; `tokens_per_s` is tokens per step over the
 same time.  The `roofline` object covers the kernel that moves the most bytes
 (combine): its algorithmic bytes per launch over its mean launch time measured
-with HIP events on the launch stream inside the timed region.  `cpu_baseline`
+with HIP events on the launch stream around the combine of every 10th step
+inside the timed region.  `--graph` replays each step as a captured HIP graph
+(split in two on the steps whose combine is bracketed by events) instead of
+eager launches.  `cpu_baseline`
 times the CPU oracle (single-threaded C) on the same workload.
 """
 
@@ -54,6 +57,8 @@ def parse():
                    help="buffer sets rotated across steps (0 = enough to exceed 2 GiB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
+    p.add_argument("--graph", action="store_true",
+                   help="replay each step as a captured HIP graph instead of eager launches")
     p.add_argument("--copy-probe", action="store_true",
                    help="run only a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -193,6 +198,7 @@ def main():
         ex = torch.empty((cap, w.hidden), dtype=torch.uint8 if w.fp8 else torch.bfloat16,
                          device=dev)
         bufs.append({
+            "index": i,
             "x": x0 if i == 0 else x0.clone(),
             "y": ex if y0 is None else (y0 if i == 0 else y0.clone()),
             "y_codes": None if yc0 is None else (yc0 if i == 0 else yc0.clone()),
@@ -245,6 +251,40 @@ def main():
     for i in range(args.warmup):
         step(bufs[i % sets])
     torch.cuda.synchronize()
+
+    if args.graph:
+        # Per buffer set: one graph of the whole step, replayed on ordinary
+        # steps, and the same step split in two (layout + dispatch, then
+        # combine) for the steps whose combine launch is bracketed by events.
+        # No call allocates or enqueues a memset when its outputs are given.
+        graphs = []
+        for b in bufs:
+            whole, front, back = (torch.cuda.CUDAGraph() for _ in range(3))
+            with torch.cuda.graph(whole):
+                lay = layout(b)
+                dispatch(b, lay)
+                combine(b, lay)
+            with torch.cuda.graph(front):
+                lay = layout(b)
+                dispatch(b, lay)
+            with torch.cuda.graph(back):
+                combine(b, lay)
+            graphs.append((whole, front, back))
+        torch.cuda.synchronize()
+
+        def step(b, ev=None):
+            whole, front, back = graphs[b["index"]]
+            if ev is None:
+                whole.replay()
+                return
+            front.replay()
+            ev[0].record(stream)
+            back.replay()
+            ev[1].record(stream)
+
+        for i in range(sets):
+            step(bufs[i])
+        torch.cuda.synchronize()
 
     # Timed region: K steps on the host clock.  HIP events on the launch stream
     # bracket the combine launch of every EVENT_EVERY-th step (each event
@@ -301,6 +341,7 @@ def main():
                    "topk": w.topk, "routing": w.routing + (f"(alpha={w.alpha})"
                                                            if w.routing == "zipf" else ""),
                    "align": w.align, "capacity_rows": cap, "buffer_sets": sets,
+                   "launch": "hip graph per step" if args.graph else "eager",
                    "combine_input": "e4m3 + fp32 scales" if fp8_combine else "bf16",
                    "replicas": ({"hot_experts": args.replicas, "per_hot": 4,
                                  "physical": n_phys} if args.replicas > 0 else None),
