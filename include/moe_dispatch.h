@@ -6,8 +6,9 @@
  * operators documented on the torch_npu API reference page for
  * npu_moe_distribute_combine (Ascend): the dispatch side lays token rows out
  * expert-contiguously and returns expand_idx and the send counts in
- * prefix-sum form; the combine side "returns along the same path" and forms
- * the weighted sum of the formula in that page's 计算公式 (formula) section.
+ * prefix-sum form; the combine side retraces that path back to token order
+ * and forms the weighted sum of the formula in that page's 计算公式 (formula)
+ * section.
  * With one device the page's ReduceScatterV (tensor-parallel) and AlltoAllv
  * (expert-parallel) exchanges are identities: the whole expert set is the one
  * expert-parallel rank's share.
@@ -192,8 +193,9 @@ int moe_dispatch_layout_replicated(const int32_t* expert_ids, int32_t bs, int32_
  * (function description: combine retraces the dispatch path); expand_x is
  * that page's (max(tp,1)*A, H) input, here [capacity_rows, hidden].  With
  * out_dtype MOE_FP8_E4M3 the rows are quantised on the way, the page's
- * comm_quant_mode "quantised transfer" (its dtype is unreadable on the page;
- * e4m3fn with per-128-channel scales is this library's reading).
+ * comm_quant_mode option for a quantised transfer (its dtype is unreadable
+ * on the page; e4m3fn with per-128-channel scales is this library's
+ * reading).
  *
  *  x              in  bf16 [bs, hidden], row stride x_stride (>= hidden);
  *                     base 16-byte aligned, x_stride*2 a multiple of 16.
