@@ -185,3 +185,18 @@ def test_layout_replicated_rules(lib):
                                               FAKE, FAKE, None, None, 0, None) == 1
     assert lib.moe_dispatch_layout_replicated(FAKE, 4, 2, 8, FAKE, FAKE, 513, 0, 128, FAKE,
                                               FAKE, FAKE, FAKE, None, None, 0, None) == 1
+
+
+def test_plain_c_program_uses_the_abi(tmp_path):
+    """The header compiles as C99 and a C program links the library and gets
+    the documented results from every host-side call (no GPU needed)."""
+    import combine_moe_dispatch_layout_amd as m
+    lib = m.library_path()
+    exe = tmp_path / "abi_host_check"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic",
+                    "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c", "abi_host_check.c"), "-o", str(exe),
+                    lib, f"-Wl,-rpath,{os.path.dirname(lib)}"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert out.stdout.strip() == "ok"
