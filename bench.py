@@ -7,16 +7,17 @@ expert-contiguous, 128-row-padded buffer) -> moe_combine (weighted gather-sum
 + shared row).  Inputs are seeded synthetic tensors already resident in HBM
 when the timed region starts.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload skewed] [--graph]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload skewed] [--graph] [--fused]
 
 `value` is algorithmic bytes per step (real rows only, never padding) divided
 by the measured step time, in GB/s; `tokens_per_s` is tokens per step over the
 same time.  The `roofline` object covers the kernel that moves the most bytes
 (combine): its algorithmic bytes per launch over its mean launch time measured
 with HIP events on the launch stream around the combine of every 10th step
-inside the timed region.  `--graph` replays each step as a captured HIP graph
-(split in two on the steps whose combine is bracketed by events) instead of
-eager launches.  `cpu_baseline`
+inside the timed region.  `--graph` replays the steps as captured HIP graphs
+of 10 steps each (split before the combine that the events bracket) instead
+of eager launches; `--fused` runs layout + dispatch through moe_dispatch_fused
+(one launch for bf16 batches of at most 2048 pairs).  `cpu_baseline`
 times the CPU oracle (single-threaded C) on the same workload.
 """
 
@@ -25,6 +26,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -57,8 +59,12 @@ def parse():
                    help="buffer sets rotated across steps (0 = enough to exceed 2 GiB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
+    p.add_argument("--fused", action="store_true",
+                   help="layout + dispatch through moe_dispatch_fused (one launch for bf16 "
+                        "batches of at most 2048 pairs)")
     p.add_argument("--graph", action="store_true",
-                   help="replay each step as a captured HIP graph instead of eager launches")
+                   help="replay the steps as captured HIP graphs of 10 steps instead of eager "
+                        "launches")
     p.add_argument("--copy-probe", action="store_true",
                    help="run only a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -154,6 +160,10 @@ def main():
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               "(the path is single-device; no collectives are built)", file=sys.stderr)
         sys.exit(2)
+    if args.fused and args.replicas > 0:
+        print("--fused takes logical expert ids; it does not combine with --replicas",
+              file=sys.stderr)
+        sys.exit(2)
     import torch
     if args.copy_probe:
         copy_probe()
@@ -239,9 +249,20 @@ def main():
             moe.moe_combine(b["y"], route_ids, lay.expand_idx, lay.ep_send_counts, scales,
                             b["shared"], n_phys, out=b["out"])
 
-    def step(b, ev=None):
+    def front(b):
+        """Layout and dispatch of one step; returns the layout."""
+        if args.fused:
+            moe.moe_dispatch_fused(b["x"], ids, n_phys, w.align, out=b["layout"],
+                                   capacity_rows=cap, expand_x=b["expand_x"],
+                                   out_dtype="fp8" if w.fp8 else "bf16",
+                                   quant_scales=b["scales"], workspace=ws)
+            return b["layout"]
         lay = layout(b)
         dispatch(b, lay)
+        return lay
+
+    def step(b, ev=None):
+        lay = front(b)
         if ev is not None:
             ev[0].record(stream)
         combine(b, lay)
@@ -252,38 +273,33 @@ def main():
         step(bufs[i % sets])
     torch.cuda.synchronize()
 
+    graphs = None
     if args.graph:
-        # Per buffer set: one graph of the whole step, replayed on ordinary
-        # steps, and the same step split in two (layout + dispatch, then
-        # combine) for the steps whose combine launch is bracketed by events.
-        # No call allocates or enqueues a memset when its outputs are given.
+        # Steps are captured EVENT_EVERY at a time, the way a serving loop
+        # replays a whole pass: graph A holds EVENT_EVERY - 1 whole steps and
+        # the layout + dispatch of the last one, graph B that last step's
+        # combine, so its launch can be bracketed by events on the stream.
+        # One pattern per distinct sequence of buffer sets.  No call
+        # allocates or enqueues a memset when its outputs are given.
+        if args.steps % EVENT_EVERY:
+            print(f"--graph needs --steps to be a multiple of {EVENT_EVERY}", file=sys.stderr)
+            sys.exit(2)
         graphs = []
-        for b in bufs:
-            whole, front, back = (torch.cuda.CUDAGraph() for _ in range(3))
-            with torch.cuda.graph(whole):
-                lay = layout(b)
-                dispatch(b, lay)
-                combine(b, lay)
-            with torch.cuda.graph(front):
-                lay = layout(b)
-                dispatch(b, lay)
+        for c in range(sets // math.gcd(sets, EVENT_EVERY)):
+            first = c * EVENT_EVERY
+            head, back = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(head):
+                for j in range(EVENT_EVERY - 1):
+                    b = bufs[(first + j) % sets]
+                    combine(b, front(b))
+                b = bufs[(first + EVENT_EVERY - 1) % sets]
+                lay = front(b)
             with torch.cuda.graph(back):
                 combine(b, lay)
-            graphs.append((whole, front, back))
-        torch.cuda.synchronize()
-
-        def step(b, ev=None):
-            whole, front, back = graphs[b["index"]]
-            if ev is None:
-                whole.replay()
-                return
-            front.replay()
-            ev[0].record(stream)
+            graphs.append((head, back))
+        for head, back in graphs:
+            head.replay()
             back.replay()
-            ev[1].record(stream)
-
-        for i in range(sets):
-            step(bufs[i])
         torch.cuda.synchronize()
 
     # Timed region: K steps on the host clock.  HIP events on the launch stream
@@ -293,8 +309,17 @@ def main():
               for i in range(0, args.steps, EVENT_EVERY)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(bufs[i % sets], events.get(i))
+    if graphs is None:
+        for i in range(args.steps):
+            step(bufs[i % sets], events.get(i))
+    else:
+        for c in range(args.steps // EVENT_EVERY):
+            head, back = graphs[c % len(graphs)]
+            ev = events[c * EVENT_EVERY]
+            head.replay()
+            ev[0].record(stream)
+            back.replay()
+            ev[1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     com_ms = [e[0].elapsed_time(e[1]) for e in events.values()]
@@ -305,9 +330,13 @@ def main():
     for i, e in enumerate(brk):
         b = bufs[i % sets]
         e[0].record(stream)
-        lay = layout(b)
-        e[1].record(stream)
-        dispatch(b, lay)
+        if args.fused:
+            lay = front(b)
+            e[1].record(stream)
+        else:
+            lay = layout(b)
+            e[1].record(stream)
+            dispatch(b, lay)
         e[2].record(stream)
         combine(b, lay)
         e[3].record(stream)
@@ -341,16 +370,22 @@ def main():
                    "topk": w.topk, "routing": w.routing + (f"(alpha={w.alpha})"
                                                            if w.routing == "zipf" else ""),
                    "align": w.align, "capacity_rows": cap, "buffer_sets": sets,
-                   "launch": "hip graph per step" if args.graph else "eager",
+                   "launch": (f"hip graphs of {EVENT_EVERY} steps" if args.graph else "eager"),
+                   "layout_dispatch": "moe_dispatch_fused" if args.fused else "separate",
                    "combine_input": "e4m3 + fp32 scales" if fp8_combine else "bf16",
                    "replicas": ({"hot_experts": args.replicas, "per_hot": 4,
                                  "physical": n_phys} if args.replicas > 0 else None),
                    "bytes_per_step": step_bytes},
-        "kernels_ms": {"layout": round(mean(lay_ms), 4), "dispatch": round(mean(dis_ms), 4),
-                       "combine": round(mean(com_ms), 4)},
-        "kernels_gbs": {"layout": round(nbytes["layout"] / mean(lay_ms) / 1e6, 1),
-                        "dispatch": round(nbytes["dispatch"] / mean(dis_ms) / 1e6, 1),
-                        "combine": round(achieved, 1)},
+        "kernels_ms": ({"layout+dispatch (fused)": round(mean(lay_ms), 4),
+                        "combine": round(mean(com_ms), 4)} if args.fused else
+                       {"layout": round(mean(lay_ms), 4), "dispatch": round(mean(dis_ms), 4),
+                        "combine": round(mean(com_ms), 4)}),
+        "kernels_gbs": ({"layout+dispatch (fused)":
+                         round((nbytes["layout"] + nbytes["dispatch"]) / mean(lay_ms) / 1e6, 1),
+                         "combine": round(achieved, 1)} if args.fused else
+                        {"layout": round(nbytes["layout"] / mean(lay_ms) / 1e6, 1),
+                         "dispatch": round(nbytes["dispatch"] / mean(dis_ms) / 1e6, 1),
+                         "combine": round(achieved, 1)}),
         "roofline": {"kernel": "combine_fp8" if fp8_combine else "combine", "bound": "hbm",
                      "timed_launches": len(com_ms), "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",

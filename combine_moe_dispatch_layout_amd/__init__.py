@@ -12,6 +12,9 @@ Entry points (same names as the C ABI):
   ``Layout(expert_counts, ep_send_counts, expand_idx, status)``
 * ``moe_dispatch(x, expert_ids, layout_or_arrays..., out_dtype="bf16")`` ->
   ``expand_x`` (and ``quant_scales`` for e4m3)
+* ``moe_dispatch_fused(x, expert_ids, num_experts, align=128)`` ->
+  ``(Layout, expand_x)`` (and ``quant_scales`` for e4m3): layout + dispatch in
+  one call, one kernel launch for bf16 batches of at most 2048 pairs
 * ``moe_combine(expand_x, expert_ids, expand_idx, ep_send_counts,
   expert_scales, shared_expert_x)`` -> ``x_out``
 * ``moe_combine_fp8(expand_x_codes, quant_scales, ...)`` -> ``x_out`` (expert
@@ -39,7 +42,7 @@ __all__ = [
     "MoeError", "Layout", "library_path", "load_library",
     "moe_dispatch_capacity", "moe_dispatch_layout_workspace_size",
     "moe_dispatch_layout", "moe_dispatch_layout_ep", "moe_dispatch_layout_replicated",
-    "moe_dispatch", "moe_combine", "moe_plan_compensation",
+    "moe_dispatch", "moe_dispatch_fused", "moe_combine", "moe_plan_compensation",
     "moe_combine_fp8",
     "MOE_BF16", "MOE_FP8_E4M3", "MOE_FLAG_ID_RANGE", "MOE_FLAG_DUP_ID", "MOE_FLAG_GUARD",
 ]
@@ -83,6 +86,8 @@ def load_library() -> ctypes.CDLL:
         "moe_dispatch_layout": (ctypes.c_int, [P, i32, i32, i32, i32, P, P, P, P, P, sz, P]),
         "moe_dispatch": (ctypes.c_int, [P, i64, i32, i32, P, P, P, i32, i32, P, i64, i64, i32,
                                         P, P, P]),
+        "moe_dispatch_fused": (ctypes.c_int, [P, i64, i32, i32, P, i32, i32, i32, P, P, P, P,
+                                              i64, i64, i32, P, P, P, sz, P]),
         "moe_combine": (ctypes.c_int, [P, i64, i64, P, P, P, P, P, i64, i32, i32, i32, i32, P,
                                        P, P]),
         "moe_combine_fp8": (ctypes.c_int, [P, i64, i64, P, P, P, P, P, P, i64, i32, i32, i32,
@@ -208,6 +213,52 @@ def moe_dispatch(x: torch.Tensor, expert_ids: torch.Tensor, expand_idx: torch.Te
         _ptr(status), _stream(x))
     _check(rc)
     return expand_x if dtype == MOE_BF16 else (expand_x, quant_scales)
+
+
+def moe_dispatch_fused(x: torch.Tensor, expert_ids: torch.Tensor, num_experts: int,
+                       align: int = 128, *, out: Optional[Layout] = None,
+                       capacity_rows: Optional[int] = None, out_dtype: str = "bf16",
+                       expand_x: Optional[torch.Tensor] = None,
+                       quant_scales: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None):
+    """moe_dispatch_layout + moe_dispatch in one call (one launch for bf16
+    batches of at most 2048 pairs).  Returns ``(layout, expand_x)`` or
+    ``(layout, expand_x, quant_scales)``."""
+    _need(x, torch.bfloat16, "x", contiguous=False)
+    _need(expert_ids, torch.int32, "expert_ids")
+    if expert_ids.dim() != 2 or expert_ids.shape[0] != x.shape[0]:
+        raise ValueError("expert_ids must be [BS, K] with BS = x.shape[0]")
+    bs, hidden = x.shape
+    k = expert_ids.shape[1]
+    dev = x.device
+    dtype = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "e4m3": MOE_FP8_E4M3}[out_dtype]
+    if out is None:
+        out = Layout(torch.empty(num_experts, dtype=torch.int32, device=dev),
+                     torch.empty(num_experts + 1, dtype=torch.int32, device=dev),
+                     torch.empty(bs * k, dtype=torch.int32, device=dev),
+                     torch.empty(1, dtype=torch.int32, device=dev))
+    if capacity_rows is None:
+        capacity_rows = (expand_x.shape[0] if expand_x is not None
+                         else moe_dispatch_capacity(bs, k, num_experts, align))
+    if expand_x is None:
+        expand_x = torch.empty((capacity_rows, hidden),
+                               dtype=torch.bfloat16 if dtype == MOE_BF16 else torch.uint8,
+                               device=dev)
+    if dtype == MOE_FP8_E4M3 and quant_scales is None:
+        quant_scales = torch.empty((capacity_rows, hidden // 128), dtype=torch.float32,
+                                   device=dev)
+    ws_bytes = moe_dispatch_layout_workspace_size(bs, k, num_experts)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    rc = load_library().moe_dispatch_fused(
+        _ptr(x), _row_stride(x, "x"), bs, hidden, _ptr(expert_ids), k, num_experts, align,
+        _ptr(out.expert_counts), _ptr(out.ep_send_counts), _ptr(out.expand_idx),
+        _ptr(expand_x), _row_stride(expand_x, "expand_x"), capacity_rows, dtype,
+        _ptr(quant_scales) if dtype == MOE_FP8_E4M3 else None, _ptr(out.status),
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(x))
+    _check(rc)
+    return (out, expand_x) if dtype == MOE_BF16 else (out, expand_x, quant_scales)
 
 
 def moe_combine(expand_x: torch.Tensor, expert_ids: torch.Tensor, expand_idx: torch.Tensor,

@@ -164,15 +164,65 @@ int moe_dispatch(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
   if (expert_ids == nullptr || expand_idx == nullptr || ep_send_counts == nullptr)
     return MOE_ERR_INVALID_ARG;
   if (!row_ok(x, x_stride, hidden, 2)) return MOE_ERR_INVALID_ARG;
+  // With no capacity nothing is written (every pair is guarded), so the
+  // output buffers may be absent.
   const int out_elem = out_dtype == MOE_BF16 ? 2 : 1;
-  if (!row_ok(expand_x, expand_x_stride, hidden, out_elem)) return MOE_ERR_INVALID_ARG;
+  if (capacity_rows > 0 && !row_ok(expand_x, expand_x_stride, hidden, out_elem))
+    return MOE_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (out_dtype == MOE_BF16)
     return hip_status(moe::launch_dispatch_bf16(x, x_stride, bs, hidden, expert_ids, expand_idx,
                                                 ep_send_counts, k, num_experts, expand_x,
                                                 expand_x_stride, capacity_rows, status, s));
-  if (quant_scales == nullptr || (reinterpret_cast<uintptr_t>(quant_scales) & 3u) != 0)
+  if (capacity_rows > 0 &&
+      (quant_scales == nullptr || (reinterpret_cast<uintptr_t>(quant_scales) & 3u) != 0))
     return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_dispatch_fp8(x, x_stride, bs, hidden, expert_ids, expand_idx,
+                                             ep_send_counts, k, num_experts, expand_x,
+                                             expand_x_stride, capacity_rows, quant_scales,
+                                             status, s));
+}
+
+int moe_dispatch_fused(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
+                       const int32_t* expert_ids, int32_t k, int32_t num_experts, int32_t align,
+                       int32_t* expert_counts, int32_t* ep_send_counts, int32_t* expand_idx,
+                       void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
+                       int32_t out_dtype, float* quant_scales, int32_t* status, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  if (!layout_args_ok(bs, k, num_experts, align)) return MOE_ERR_INVALID_ARG;
+  if (hidden <= 0 || hidden % 32 != 0 || hidden > 65536) return MOE_ERR_INVALID_ARG;
+  if (out_dtype == MOE_FP8_E4M3 && hidden % 128 != 0) return MOE_ERR_INVALID_ARG;
+  if (capacity_rows < 0 || !rows_fit(bs, hidden)) return MOE_ERR_INVALID_ARG;
+  if (expert_counts == nullptr || ep_send_counts == nullptr) return MOE_ERR_INVALID_ARG;
+  if (bs > 0) {
+    if (expert_ids == nullptr || expand_idx == nullptr) return MOE_ERR_INVALID_ARG;
+    if (!row_ok(x, x_stride, hidden, 2)) return MOE_ERR_INVALID_ARG;
+    if (capacity_rows > 0 &&
+        !row_ok(expand_x, expand_x_stride, hidden, out_dtype == MOE_BF16 ? 2 : 1))
+      return MOE_ERR_INVALID_ARG;
+    if (capacity_rows > 0 && out_dtype == MOE_FP8_E4M3 &&
+        (quant_scales == nullptr || (reinterpret_cast<uintptr_t>(quant_scales) & 3u) != 0))
+      return MOE_ERR_INVALID_ARG;
+  }
+  const moe::LayoutPlan plan = moe::plan_layout(bs, k);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (bs > 0 && out_dtype == MOE_BF16 && plan.n_pairs <= moe::kFusedMaxPairs)
+    return hip_status(moe::launch_dispatch_fused_bf16(
+        x, x_stride, bs, hidden, expert_ids, k, num_experts, align, expert_counts,
+        ep_send_counts, expand_idx, status, expand_x, expand_x_stride, capacity_rows, s));
+  // Otherwise: the layout launch(es), then the scatter, on the same stream.
+  const size_t need = moe::layout_workspace_bytes(plan, num_experts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return MOE_ERR_WORKSPACE;
+  hipError_t err = moe::launch_layout(expert_ids, k, num_experts, align, plan, expert_counts,
+                                      ep_send_counts, expand_idx, status, workspace,
+                                      moe::ReplicaMap{}, moe::RankSplit{}, s);
+  if (err != hipSuccess || bs == 0) return hip_status(err);
+  if (out_dtype == MOE_BF16)
+    return hip_status(moe::launch_dispatch_bf16(x, x_stride, bs, hidden, expert_ids, expand_idx,
+                                                ep_send_counts, k, num_experts, expand_x,
+                                                expand_x_stride, capacity_rows, status, s));
   return hip_status(moe::launch_dispatch_fp8(x, x_stride, bs, hidden, expert_ids, expand_idx,
                                              ep_send_counts, k, num_experts, expand_x,
                                              expand_x_stride, capacity_rows, quant_scales,

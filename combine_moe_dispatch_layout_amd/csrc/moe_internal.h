@@ -176,6 +176,17 @@ hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int
                          int32_t* expand_idx, int32_t* status, void* workspace,
                          const ReplicaMap& map, const RankSplit& ranks, hipStream_t stream);
 
+// Batches of at most this many pairs fit one layout workgroup; the fused
+// layout + bf16 scatter derives the layout in every scatter workgroup.
+constexpr int kFusedMaxPairs = kLayoutThreads * kLayoutSingleMaxRounds;
+
+hipError_t launch_dispatch_fused_bf16(const void* x, int64_t x_stride, int32_t bs,
+                                      int32_t hidden, const int32_t* ids, int32_t k,
+                                      int32_t num_experts, int32_t align, int32_t* counts,
+                                      int32_t* send, int32_t* expand_idx, int32_t* status,
+                                      void* expand_x, int64_t expand_x_stride,
+                                      int64_t capacity_rows, hipStream_t stream);
+
 // ---- dispatch / combine -----------------------------------------------------
 hipError_t launch_dispatch_bf16(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
                                 const int32_t* ids, const int32_t* expand_idx,

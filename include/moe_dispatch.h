@@ -208,6 +208,8 @@ int moe_dispatch_layout_replicated(const int32_t* expert_ids, int32_t bs, int32_
  *                     bytes a multiple of 16.  Row slot(t,j) receives token t
  *                     for every pair j.  Padding rows are NOT written.
  *  capacity_rows  in  rows of expand_x (size it with moe_dispatch_capacity).
+ *                     With 0 rows every pair is guarded and nothing is
+ *                     written; expand_x and quant_scales may then be NULL.
  *  quant_scales   out fp32 [capacity_rows, hidden/128] row-major when
  *                     out_dtype is MOE_FP8_E4M3 (else ignored, may be NULL):
  *                     s = amax/448 over the 128 channels of the block;
@@ -222,6 +224,34 @@ int moe_dispatch(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
                  const int32_t* ep_send_counts, int32_t k, int32_t num_experts, void* expand_x,
                  int64_t expand_x_stride, int64_t capacity_rows, int32_t out_dtype,
                  float* quant_scales, int32_t* status, void* stream);
+
+/*
+ * Layout and dispatch in one call: the results of moe_dispatch_layout
+ * followed by moe_dispatch on the same stream, bit for bit (outputs, padding
+ * rows left unwritten, status bits).  For decode-sized batches (bs*k <= 2048)
+ * with bf16 output it is a single kernel launch: every scatter workgroup
+ * derives the whole layout from the ids in on-chip memory, so no separate
+ * layout launch or wait precedes the scatter (the TEMPO summary, section 2,
+ * folds count gathering into the dispatch kernel; here the counts, offsets
+ * and ranks are folded in).  Larger batches and e4m3 output run the layout
+ * and dispatch kernels in sequence.
+ *
+ *  x, x_stride, bs, hidden                   as for moe_dispatch.
+ *  expert_ids, k, num_experts, align         as for moe_dispatch_layout.
+ *  expert_counts, ep_send_counts, expand_idx out, as for moe_dispatch_layout.
+ *  expand_x, expand_x_stride, capacity_rows, out_dtype, quant_scales
+ *                                            as for moe_dispatch.
+ *  status         out int32 [1] or NULL: MOE_FLAG_ID_RANGE | MOE_FLAG_DUP_ID |
+ *                     MOE_FLAG_GUARD of this call, overwritten.
+ *  workspace      as for moe_dispatch_layout (unused, may be NULL, when the
+ *                     single launch applies).
+ */
+int moe_dispatch_fused(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
+                       const int32_t* expert_ids, int32_t k, int32_t num_experts, int32_t align,
+                       int32_t* expert_counts, int32_t* ep_send_counts, int32_t* expand_idx,
+                       void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
+                       int32_t out_dtype, float* quant_scales, int32_t* status, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /*
  * Combine: gather each token's K expert-output rows back and form

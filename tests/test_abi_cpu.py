@@ -200,3 +200,22 @@ def test_plain_c_program_uses_the_abi(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0, out.stdout + out.stderr
     assert out.stdout.strip() == "ok"
+
+
+def test_dispatch_fused_rules(lib):
+    def call(x=FAKE, xs=64, bs=4, h=64, ids=FAKE, k=2, e=8, align=128, counts=FAKE, send=FAKE,
+             idx=FAKE, ex=FAKE, es=64, cap=64, dtype=0, qs=None, ws=None, wsb=0):
+        return lib.moe_dispatch_fused(x, xs, bs, h, ids, k, e, align, counts, send, idx, ex, es,
+                                      cap, dtype, qs, None, ws, wsb, None)
+
+    assert call(dtype=5) == 3              # unknown dtype
+    assert call(k=9) == 1                  # k > num_experts
+    assert call(align=3) == 1              # align not a power of two
+    assert call(h=48, xs=48, es=48) == 1   # hidden % 32
+    assert call(dtype=1) == 1              # e4m3 needs hidden % 128 and scales
+    assert call(h=128, xs=128, es=128, dtype=1) == 1   # e4m3 without scales
+    assert call(counts=None) == 1
+    assert call(x=FAKE + 2) == 1           # misaligned rows
+    assert call(cap=-1) == 1
+    # beyond one workgroup's pairs the two-launch path needs the workspace
+    assert call(bs=4096, k=8, e=256) == 2
