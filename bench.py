@@ -17,7 +17,7 @@ with HIP events on the launch stream around the combine of every 10th step
 inside the timed region.  `--graph` replays the steps as captured HIP graphs
 of 10 steps each (split before the combine that the events bracket) instead
 of eager launches; `--fused` runs layout + dispatch through moe_dispatch_fused
-(one launch for bf16 batches of at most 2048 pairs).  `cpu_baseline`
+(one launch for batches of at most 2048 pairs).  `cpu_baseline`
 times the CPU oracle (single-threaded C) on the same workload.
 """
 
@@ -60,7 +60,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
     p.add_argument("--fused", action="store_true",
-                   help="layout + dispatch through moe_dispatch_fused (one launch for bf16 "
+                   help="layout + dispatch through moe_dispatch_fused (one launch for "
                         "batches of at most 2048 pairs)")
     p.add_argument("--graph", action="store_true",
                    help="replay the steps as captured HIP graphs of 10 steps instead of eager "

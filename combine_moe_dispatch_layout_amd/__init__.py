@@ -14,7 +14,7 @@ Entry points (same names as the C ABI):
   ``expand_x`` (and ``quant_scales`` for e4m3)
 * ``moe_dispatch_fused(x, expert_ids, num_experts, align=128)`` ->
   ``(Layout, expand_x)`` (and ``quant_scales`` for e4m3): layout + dispatch in
-  one call, one kernel launch for bf16 batches of at most 2048 pairs
+  one call, one kernel launch for batches of at most 2048 pairs
 * ``moe_combine(expand_x, expert_ids, expand_idx, ep_send_counts,
   expert_scales, shared_expert_x)`` -> ``x_out``
 * ``moe_combine_fp8(expand_x_codes, quant_scales, ...)`` -> ``x_out`` (expert
@@ -221,8 +221,8 @@ def moe_dispatch_fused(x: torch.Tensor, expert_ids: torch.Tensor, num_experts: i
                        expand_x: Optional[torch.Tensor] = None,
                        quant_scales: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None):
-    """moe_dispatch_layout + moe_dispatch in one call (one launch for bf16
-    batches of at most 2048 pairs).  Returns ``(layout, expand_x)`` or
+    """moe_dispatch_layout + moe_dispatch in one call (one launch for batches
+    of at most 2048 pairs).  Returns ``(layout, expand_x)`` or
     ``(layout, expand_x, quant_scales)``."""
     _need(x, torch.bfloat16, "x", contiguous=False)
     _need(expert_ids, torch.int32, "expert_ids")

@@ -207,10 +207,16 @@ int moe_dispatch_fused(const void* x, int64_t x_stride, int32_t bs, int32_t hidd
   }
   const moe::LayoutPlan plan = moe::plan_layout(bs, k);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (bs > 0 && out_dtype == MOE_BF16 && plan.n_pairs <= moe::kFusedMaxPairs)
-    return hip_status(moe::launch_dispatch_fused_bf16(
+  if (bs > 0 && plan.n_pairs <= moe::kFusedMaxPairs) {
+    if (out_dtype == MOE_BF16)
+      return hip_status(moe::launch_dispatch_fused_bf16(
+          x, x_stride, bs, hidden, expert_ids, k, num_experts, align, expert_counts,
+          ep_send_counts, expand_idx, status, expand_x, expand_x_stride, capacity_rows, s));
+    return hip_status(moe::launch_dispatch_fused_fp8(
         x, x_stride, bs, hidden, expert_ids, k, num_experts, align, expert_counts,
-        ep_send_counts, expand_idx, status, expand_x, expand_x_stride, capacity_rows, s));
+        ep_send_counts, expand_idx, status, expand_x, expand_x_stride, capacity_rows,
+        quant_scales, s));
+  }
   // Otherwise: the layout launch(es), then the scatter, on the same stream.
   const size_t need = moe::layout_workspace_bytes(plan, num_experts);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))

@@ -79,35 +79,8 @@ __global__ __launch_bounds__(THREADS) void dispatch_fp8_kernel(
   resolve_routes<KMAX>(meta, send_lds, k, E, cap, slot, unused_w, status,
                        threadIdx.x < kWave && chunk == 0);
 
-  float f[16];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    f[2 * c] = bf16lo_to_f32(a[c]);
-    f[2 * c + 1] = bf16hi_to_f32(a[c]);
-    f[8 + 2 * c] = bf16lo_to_f32(b[c]);
-    f[8 + 2 * c + 1] = bf16hi_to_f32(b[c]);
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(f[c]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
-  amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
-
-  const float s = amax / 448.0f;  // IEEE division (correctly rounded)
-  u32x4 codes = {0u, 0u, 0u, 0u};
-  if (amax != 0.0f) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float q0 = __builtin_amdgcn_fmed3f(f[4 * c + 0] / s, 448.0f, -448.0f);
-      const float q1 = __builtin_amdgcn_fmed3f(f[4 * c + 1] / s, 448.0f, -448.0f);
-      const float q2 = __builtin_amdgcn_fmed3f(f[4 * c + 2] / s, 448.0f, -448.0f);
-      const float q3 = __builtin_amdgcn_fmed3f(f[4 * c + 3] / s, 448.0f, -448.0f);
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);
-      codes[c] = (uint32_t)w;
-    }
-  }
+  float s;
+  const u32x4 codes = quantize16_e4m3(a, b, s);
 
   // Code rows are written with streaming stores (each wave covers whole
   // lines).  A wave holds only 32 bytes of a scale row, so scale stores stay

@@ -122,6 +122,47 @@ __device__ __forceinline__ void resolve_routes(const PairMeta& m, const int* sen
   }
 }
 
+// e4m3 quantisation of 16 consecutive bf16 channels held in two 16-byte
+// vectors.  The 8 lanes of an aligned lane octet hold one 128-channel block
+// and share its scale s = amax / 448 (a correctly rounded division); each
+// code is e4m3(x / s), rounded to nearest even by the hardware conversion
+// after an exact clamp to +-448.  An all-zero block gives s = 0 and zero
+// codes.  Every lane of the wave must take part (the maxima are exchanged
+// across lanes); lanes without data pass zeros.
+__device__ __forceinline__ u32x4 quantize16_e4m3(const u32x4& a, const u32x4& b, float& s_out) {
+  float f[16];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    f[2 * c] = bf16lo_to_f32(a[c]);
+    f[2 * c + 1] = bf16hi_to_f32(a[c]);
+    f[8 + 2 * c] = bf16lo_to_f32(b[c]);
+    f[8 + 2 * c + 1] = bf16hi_to_f32(b[c]);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(f[c]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
+
+  const float s = amax / 448.0f;  // IEEE division (correctly rounded)
+  u32x4 codes = {0u, 0u, 0u, 0u};
+  if (amax != 0.0f) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float q0 = __builtin_amdgcn_fmed3f(f[4 * c + 0] / s, 448.0f, -448.0f);
+      const float q1 = __builtin_amdgcn_fmed3f(f[4 * c + 1] / s, 448.0f, -448.0f);
+      const float q2 = __builtin_amdgcn_fmed3f(f[4 * c + 2] / s, 448.0f, -448.0f);
+      const float q3 = __builtin_amdgcn_fmed3f(f[4 * c + 3] / s, 448.0f, -448.0f);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);
+      codes[c] = (uint32_t)w;
+    }
+  }
+  s_out = s;
+  return codes;
+}
+
 // Copies ep_send_counts[0..E] into LDS (one pass per workgroup).
 __device__ __forceinline__ void stage_send(int* send_lds, const int32_t* __restrict__ send,
                                            int32_t E) {
@@ -179,6 +220,14 @@ hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int
 // Batches of at most this many pairs fit one layout workgroup; the fused
 // layout + bf16 scatter derives the layout in every scatter workgroup.
 constexpr int kFusedMaxPairs = kLayoutThreads * kLayoutSingleMaxRounds;
+
+hipError_t launch_dispatch_fused_fp8(const void* x, int64_t x_stride, int32_t bs,
+                                     int32_t hidden, const int32_t* ids, int32_t k,
+                                     int32_t num_experts, int32_t align, int32_t* counts,
+                                     int32_t* send, int32_t* expand_idx, int32_t* status,
+                                     void* expand_x, int64_t expand_x_stride,
+                                     int64_t capacity_rows, float* quant_scales,
+                                     hipStream_t stream);
 
 hipError_t launch_dispatch_fused_bf16(const void* x, int64_t x_stride, int32_t bs,
                                       int32_t hidden, const int32_t* ids, int32_t k,

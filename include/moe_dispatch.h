@@ -228,13 +228,13 @@ int moe_dispatch(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
 /*
  * Layout and dispatch in one call: the results of moe_dispatch_layout
  * followed by moe_dispatch on the same stream, bit for bit (outputs, padding
- * rows left unwritten, status bits).  For decode-sized batches (bs*k <= 2048)
- * with bf16 output it is a single kernel launch: every scatter workgroup
- * derives the whole layout from the ids in on-chip memory, so no separate
- * layout launch or wait precedes the scatter (the TEMPO summary, section 2,
- * folds count gathering into the dispatch kernel; here the counts, offsets
- * and ranks are folded in).  Larger batches and e4m3 output run the layout
- * and dispatch kernels in sequence.
+ * rows left unwritten, e4m3 codes and scales, status bits).  For
+ * decode-sized batches (bs*k <= 2048) it is a single kernel launch: every
+ * scatter workgroup derives the whole layout from the ids in on-chip memory,
+ * so no separate layout launch or wait precedes the scatter (the TEMPO
+ * summary, section 2, folds count gathering into the dispatch kernel; here
+ * the counts, offsets and ranks are folded in).  Larger batches run the
+ * layout and dispatch kernels in sequence.
  *
  *  x, x_stride, bs, hidden                   as for moe_dispatch.
  *  expert_ids, k, num_experts, align         as for moe_dispatch_layout.

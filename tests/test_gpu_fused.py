@@ -4,9 +4,10 @@ the oracle's layout and bf16 dispatch.
 Bars as for the separate calls: counts, offsets, ranks and status bit-exact;
 the whole dispatched buffer bit-exact, including padding rows the call must
 leave untouched (pre-filled with the oracle's sentinel) and canary rows past
-capacity.  Batches of at most 2048 pairs take the one-launch kernel; larger
-batches and e4m3 output take the layout + dispatch launches and must equal
-the separate calls.
+capacity.  Batches of at most 2048 pairs take the one-launch kernels (bf16 and e4m3;
+e4m3 codes and scales bit-exact against the oracle's quantiser); larger
+batches take the layout + dispatch launches and must equal the separate
+calls.
 """
 
 import numpy as np
@@ -106,7 +107,8 @@ def test_two_launch_paths_equal_the_separate_calls():
     import combine_moe_dispatch_layout_amd as moe
     rng = np.random.default_rng(7)
     for bs, h, e, k, dtype in [(4097, 256, 64, 1, "bf16"), (700, 512, 64, 8, "bf16"),
-                               (100, 1024, 32, 4, "fp8"), (600, 256, 16, 8, "fp8")]:
+                               (100, 1024, 32, 4, "fp8"), (600, 256, 16, 8, "fp8"),
+                               (128, 7168, 256, 8, "fp8")]:
         ids = torch.from_numpy(random_ids(rng, bs, e, k)).to(DEV)
         x = to_dev_bf16(random_bf16(rng, (bs, h)))
         cap = moe.moe_dispatch_capacity(bs, k, e, 128)
@@ -149,3 +151,31 @@ def test_zero_capacity_writes_nothing_and_flags_every_pair():
                          out_dtype=dtype, status=st)
         torch.cuda.synchronize()
         assert int(st.cpu()[0]) == oracle.FLAG_GUARD
+
+
+@pytest.mark.parametrize("bs,h,e,k,align", [
+    (1, 128, 1, 1, 128), (16, 128, 8, 2, 128), (128, 7168, 256, 8, 128), (100, 512, 512, 16, 1),
+    (2048, 128, 64, 1, 128), (37, 4224, 40, 8, 64),
+])
+def test_one_launch_e4m3_matches_the_oracle(bs, h, e, k, align):
+    import combine_moe_dispatch_layout_amd as moe
+    rng = np.random.default_rng(bs * 13 + k)
+    ids = random_ids(rng, bs, e, k)
+    x_bits = random_bf16(rng, (bs, h))
+    x_bits[0, :128] = 0                                  # an all-zero block
+    cap = oracle.capacity(bs, k, e, align)
+    c, s, r, f = oracle.layout(ids, e, align)
+    ref_codes, ref_scales, f2 = oracle.dispatch_fp8(x_bits, ids, r, s, e, cap)
+    codes = torch.full((cap, h), oracle.SENTINEL_FP8, dtype=torch.uint8, device=DEV)
+    scales = torch.full((cap, h // 128), oracle.SENTINEL_SCALE, dtype=torch.float32, device=DEV)
+    lay, _, _ = moe.moe_dispatch_fused(to_dev_bf16(x_bits), torch.from_numpy(ids).to(DEV), e,
+                                       align, capacity_rows=cap, out_dtype="fp8", expand_x=codes,
+                                       quant_scales=scales)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(lay.expert_counts.cpu().numpy(), c)
+    np.testing.assert_array_equal(lay.ep_send_counts.cpu().numpy(), s)
+    np.testing.assert_array_equal(lay.expand_idx.cpu().numpy(), r)
+    assert int(lay.status.cpu()[0]) == (f | f2) == 0
+    np.testing.assert_array_equal(codes.cpu().numpy(), ref_codes)
+    np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32),
+                                  ref_scales.view(np.uint32))
