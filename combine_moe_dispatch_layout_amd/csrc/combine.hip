@@ -5,13 +5,13 @@
 //
 // One workgroup per item = (token, row chunk).  The workgroup stages the
 // send counts in LDS while lanes 0..K-1 fetch the token's ids / ranks /
-// weights, so the routes cost one memory round trip plus one LDS read.
-// Each thread issues the K row loads of its 16-byte vector (plus the shared
-// row) before consuming any, so K+1 independent 16-byte loads are in flight
-// per thread; the sum is an fp32 fused multiply-add chain in ascending j from
-// +0, then + shared, then one round-to-nearest-even into bf16.  y is read
-// exactly once (non-temporal loads) and x_out written once (non-temporal
-// stores).
+// weights, so the routes cost one memory round trip plus one LDS read; the
+// shared row's load does not depend on them and is issued first.  Each
+// thread then issues the K row loads of its 16-byte vector before consuming
+// any, so K+1 independent 16-byte loads are in flight per thread.  The sum
+// is an fp32 fused multiply-add chain in ascending j from +0, then + shared,
+// then one round-to-nearest-even into bf16.  y is read exactly once
+// (non-temporal loads) and x_out written once (non-temporal stores).
 #include "moe_internal.h"
 
 namespace moe {
@@ -29,24 +29,28 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(
   const int32_t chunk = blockIdx.x - t * nchunks;
   PairMeta meta;
   fetch_pair_meta(meta, t, k, ids, idx, scales);
-  stage_send(send_lds, send, E);  // overlaps the fetch above
-  int64_t slot[KMAX];
-  float w[KMAX];
-  resolve_routes<KMAX>(meta, send_lds, k, E, cap, slot, w, status,
-                       threadIdx.x < kWave && chunk == 0);
   const int32_t v0 = chunk * (THREADS * VPT) + threadIdx.x;
-
-  u32x4 yv[VPT][KMAX];
   u32x4 sv[VPT];
 #pragma unroll
   for (int jv = 0; jv < VPT; ++jv) {
     const int32_t v = v0 + jv * THREADS;
     sv[jv] = u32x4{0u, 0u, 0u, 0u};
+    if (shared && v < nvec) sv[jv] = load_stream(shared + (int64_t)t * ss + v);
+  }
+  stage_send(send_lds, send, E);  // overlaps the fetches above
+  int64_t slot[KMAX];
+  float w[KMAX];
+  resolve_routes<KMAX>(meta, send_lds, k, E, cap, slot, w, status,
+                       threadIdx.x < kWave && chunk == 0);
+
+  u32x4 yv[VPT][KMAX];
+#pragma unroll
+  for (int jv = 0; jv < VPT; ++jv) {
+    const int32_t v = v0 + jv * THREADS;
     if (v < nvec) {
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
         if (slot[j] >= 0) yv[jv][j] = load_stream(y + slot[j] * ys + v);
-      if (shared) sv[jv] = load_stream(shared + (int64_t)t * ss + v);
     }
   }
 #pragma unroll
@@ -101,13 +105,19 @@ __global__ __launch_bounds__(1024) void combine_fp8_kernel(
   const int32_t chunk = blockIdx.x - t * nchunks;
   PairMeta meta;
   fetch_pair_meta(meta, t, k, ids, idx, scales);
-  stage_send(send_lds, send, E);  // overlaps the fetch above
+  const int32_t g = chunk * (int32_t)blockDim.x + threadIdx.x;  // 16-channel group
+  // The shared row does not depend on the routes: its loads go out first.
+  u32x4 sh0 = {0u, 0u, 0u, 0u}, sh1 = {0u, 0u, 0u, 0u};
+  if (shared && g < ngroups) {
+    sh0 = load_stream(shared + (int64_t)t * ss + 2 * g);
+    sh1 = load_stream(shared + (int64_t)t * ss + 2 * g + 1);
+  }
+  stage_send(send_lds, send, E);  // overlaps the fetches above
   int64_t slot[KMAX];
   float w[KMAX];
   resolve_routes<KMAX>(meta, send_lds, k, E, cap, slot, w, status,
                        threadIdx.x < kWave && chunk == 0);
 
-  const int32_t g = chunk * (int32_t)blockDim.x + threadIdx.x;  // 16-channel group
   if (g >= ngroups) return;  // no workgroup barrier follows
   u32x4 q[KMAX];
   float s[KMAX];
@@ -116,11 +126,6 @@ __global__ __launch_bounds__(1024) void combine_fp8_kernel(
     if (slot[j] < 0) continue;
     q[j] = load_stream(y + slot[j] * ys + g);
     s[j] = yscale[slot[j] * nblk + (g >> 3)];
-  }
-  u32x4 sh0 = {0u, 0u, 0u, 0u}, sh1 = {0u, 0u, 0u, 0u};
-  if (shared) {
-    sh0 = load_stream(shared + (int64_t)t * ss + 2 * g);
-    sh1 = load_stream(shared + (int64_t)t * ss + 2 * g + 1);
   }
 
   float acc[16];
