@@ -65,6 +65,9 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="replay the steps as captured HIP graphs of 10 steps instead of eager "
                         "launches")
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the practical-ceiling probe (streaming kernels with the "
+                        "dispatch's and combine's read:write mixes)")
     p.add_argument("--copy-probe", action="store_true",
                    help="run only a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -152,6 +155,51 @@ def copy_probe():
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+
+
+def practical_ceiling(moe, w, launches=20):
+    """GB/s of the plain streaming probe with the dispatch's 1 : K and the
+    combine's (K + 1) : 1 row mixes at this workload's bf16 row size and
+    token count: all rows in order, and with the K expert-side rows randomly
+    permuted as the real layout scatters them (seeded; the token-side rows
+    stay in order).  Mean over `launches` launches bracketed by HIP events,
+    after 3 warm-up launches."""
+    import numpy as np
+    import torch
+    bs, k, row_bytes = w.bs, w.topk, 2 * w.hidden
+    cols = row_bytes // 4
+    g = np.random.default_rng(12345)
+    out = {}
+    for name, reads, writes in (("dispatch_mix", 1, k), ("combine_mix", k + 1, 1)):
+        src = torch.zeros((bs * reads, cols), dtype=torch.int32, device="cuda")
+        dst = torch.empty((bs * writes, cols), dtype=torch.int32, device="cuda")
+        perm = g.permutation(bs * k).astype(np.int32)
+        if writes > 1:   # dispatch: token rows in order, K copies to random rows
+            rows = {"dst": torch.from_numpy(perm).cuda()}
+        else:            # combine: K random expert rows, then the token's own shared row
+            idx = np.concatenate([perm.reshape(bs, k),
+                                  (bs * k + np.arange(bs, dtype=np.int32))[:, None]], axis=1)
+            rows = {"src": torch.from_numpy(np.ascontiguousarray(idx).ravel()).cuda()}
+        res = {}
+        for order in ("in_order", "random_rows"):
+            src_rows = rows.get("src") if order == "random_rows" else None
+            dst_rows = rows.get("dst") if order == "random_rows" else None
+            run = lambda: moe.moe_probe_stream_mix(src, dst, bs, reads, writes, src_rows,
+                                                   dst_rows)
+            for _ in range(3):
+                run()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(launches):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            secs = e0.elapsed_time(e1) / 1e3 / launches
+            res[order] = round(bs * (reads + writes) * row_bytes / secs / 1e9, 1)
+        out[name] = res
+        del src, dst
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -344,6 +392,12 @@ def main():
     lay_ms = [e[0].elapsed_time(e[1]) for e in brk]
     dis_ms = [e[1].elapsed_time(e[2]) for e in brk]
     mean = lambda v: sum(v) / len(v)
+
+    def pct(v):
+        """p10 / median / p90 in microseconds (nearest rank)."""
+        o = sorted(v)
+        at = lambda q: o[min(len(o) - 1, max(0, round(q * (len(o) - 1))))]
+        return [round(at(q) * 1e3, 2) for q in (0.1, 0.5, 0.9)]
     ms_per_step = elapsed * 1e3 / args.steps
     status = int(bufs[0]["layout"].status.cpu()[0])
     if status != 0:
@@ -386,6 +440,10 @@ def main():
                         {"layout": round(nbytes["layout"] / mean(lay_ms) / 1e6, 1),
                          "dispatch": round(nbytes["dispatch"] / mean(dis_ms) / 1e6, 1),
                          "combine": round(achieved, 1)}),
+        "kernels_us_p10_p50_p90": ({"layout+dispatch (fused)": pct(lay_ms),
+                                    "combine": pct(com_ms)} if args.fused else
+                                   {"layout": pct(lay_ms), "dispatch": pct(dis_ms),
+                                    "combine": pct(com_ms)}),
         "roofline": {"kernel": "combine_fp8" if fp8_combine else "combine", "bound": "hbm",
                      "timed_launches": len(com_ms), "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -394,6 +452,16 @@ def main():
                      "traffic_unit": "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
                      "algorithmic_bytes_per_launch": nbytes["combine"]},
     }
+    if not (args.no_ceiling or w.fp8 or fp8_combine):   # the probe models bf16 rows
+        ceil = practical_ceiling(moe, w)
+        result["practical_ceiling"] = {
+            "probe": "moe_probe_stream_mix: plain 16-B streaming kernel, same read:write row mix",
+            "unit": "GB/s", **ceil,
+            "combine_frac_of_random_rows": round(
+                achieved / ceil["combine_mix"]["random_rows"], 4),
+            "dispatch_frac_of_random_rows": round(
+                nbytes["dispatch"] / (mean(dis_ms) / 1e3) / 1e9
+                / ceil["dispatch_mix"]["random_rows"], 4) if not args.fused else None}
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

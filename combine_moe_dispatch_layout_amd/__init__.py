@@ -26,6 +26,8 @@ Entry points (same names as the C ABI):
 * ``moe_plan_compensation(expert_counts, ep_world_size, tile_cost,
   activation_cost)`` -> dict (host-side 128-aligned chunk-migration plan)
 * ``moe_dispatch_capacity`` / ``moe_dispatch_layout_workspace_size``
+* ``moe_probe_stream_mix`` (measurement only: a plain streaming kernel with a
+  chosen read : write row mix, for practical-ceiling figures)
 """
 
 from __future__ import annotations
@@ -43,7 +45,7 @@ __all__ = [
     "moe_dispatch_capacity", "moe_dispatch_layout_workspace_size",
     "moe_dispatch_layout", "moe_dispatch_layout_ep", "moe_dispatch_layout_replicated",
     "moe_dispatch", "moe_dispatch_fused", "moe_combine", "moe_plan_compensation",
-    "moe_combine_fp8",
+    "moe_combine_fp8", "moe_probe_stream_mix",
     "MOE_BF16", "MOE_FP8_E4M3", "MOE_FLAG_ID_RANGE", "MOE_FLAG_DUP_ID", "MOE_FLAG_GUARD",
 ]
 
@@ -96,6 +98,7 @@ def load_library() -> ctypes.CDLL:
                                                  P]),
         "moe_dispatch_layout_ep": (ctypes.c_int, [P, i32, i32, i32, i32, i32, P, P, P, P, P, P,
                                                   sz, P]),
+        "moe_probe_stream_mix": (ctypes.c_int, [P, i64, P, i64, i32, i32, i32, i32, P, P, P]),
         "moe_dispatch_layout_replicated": (ctypes.c_int, [P, i32, i32, i32, P, P, i32,
                                                           ctypes.c_uint64, i32, P, P, P, P, P, P,
                                                           sz, P]),
@@ -408,3 +411,25 @@ def moe_plan_compensation(expert_counts, ep_world_size: int, tile_cost: int,
     return {"moves": [tuple(int(v) for v in row) for row in moves[:n.value]],
             "loads": [int(v) for v in loads[:ep_world_size]], "before": before.value,
             "after": after.value, "ideal": ideal.value}
+
+
+def moe_probe_stream_mix(src: torch.Tensor, dst: torch.Tensor, items: int, reads: int,
+                         writes: int, src_rows: Optional[torch.Tensor] = None,
+                         dst_rows: Optional[torch.Tensor] = None) -> None:
+    """Measurement probe (include/moe_probe.h): item i XORs `reads` rows of
+    src into `writes` rows of dst.  src / dst are contiguous 2-D device
+    tensors whose rows are the probe's rows; src_rows / dst_rows optional
+    int32 row indices."""
+    for t, name in ((src, "src"), (dst, "dst")):
+        if not t.is_cuda or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 2-D device tensor")
+    row_bytes = src.shape[1] * src.element_size()
+    if dst.shape[1] * dst.element_size() != row_bytes:
+        raise ValueError("src and dst rows differ in size")
+    for t, name in ((src_rows, "src_rows"), (dst_rows, "dst_rows")):
+        if t is not None:
+            _need(t, torch.int32, name)
+    rc = load_library().moe_probe_stream_mix(
+        _ptr(src), src.shape[0], _ptr(dst), dst.shape[0], items, row_bytes, reads, writes,
+        _ptr(src_rows), _ptr(dst_rows), _stream(src))
+    _check(rc)

@@ -18,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libmoe_dispatch.so")
-SOURCES = ["api.hip", "layout.hip", "dispatch.hip", "fused.hip", "combine.hip", "planner.cpp"]
+SOURCES = ["api.hip", "layout.hip", "dispatch.hip", "fused.hip", "combine.hip", "probe.hip",
+           "planner.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -219,3 +219,17 @@ def test_dispatch_fused_rules(lib):
     assert call(cap=-1) == 1
     # beyond one workgroup's pairs the two-launch path needs the workspace
     assert call(bs=4096, k=8, e=256) == 2
+
+
+def test_probe_rules(lib):
+    def call(items=4, row_bytes=64, reads=1, writes=8, src_total=4, dst_total=32, src=FAKE,
+             dst=FAKE, src_rows=None, dst_rows=None):
+        return lib.moe_probe_stream_mix(src, src_total, dst, dst_total, items, row_bytes, reads,
+                                        writes, src_rows, dst_rows, None)
+
+    assert call(reads=0) == 1 and call(writes=17) == 1
+    assert call(row_bytes=24) == 1                 # not a multiple of 16
+    assert call(dst_total=31) == 1                 # contiguous writes overrun dst
+    assert call(src_total=3) == 1                  # contiguous reads overrun src
+    assert call(src=FAKE + 8) == 1                 # misaligned
+    assert call(items=0, src=None, dst=None) == 0  # nothing to do
