@@ -116,7 +116,15 @@ def _check(rc: int) -> None:
         raise MoeError(rc, load_library().moe_status_string(rc).decode())
 
 
+# The current stream's raw handle.  torch's raw getter skips building a
+# Stream object (about 0.1 us against 1.9 us per call, which matters for
+# decode-sized steps); the public API serves where it is absent.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t: torch.Tensor) -> Optional[int]:
+    if _raw_stream is not None:
+        return _raw_stream(t.device.index)
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
