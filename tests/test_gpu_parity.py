@@ -597,3 +597,38 @@ def test_layout_ep_matches_oracle(bs, e, k, ws):
         np.testing.assert_array_equal(lay.expand_idx.cpu().numpy(), r)
         np.testing.assert_array_equal(granks.cpu().numpy(), ranks)
         assert int(lay.status.cpu()[0]) == f
+
+
+# ------------------------------------------------------------ maximum sizes
+
+def test_maximum_dimensions():
+    """H = 65536 (the library's largest row), E = 512 experts and K = 16 per
+    token at once, through layout, bf16 and e4m3 dispatch, both combines and
+    the fused entry point, every element against the oracle (align 1 keeps
+    the buffers small)."""
+    rng = np.random.default_rng(65536)
+    bs, h, e, k, align = 3, 65536, 512, 16, 1
+    ids = random_ids(rng, bs, e, k)
+    x = random_bf16(rng, (bs, h))
+    x[1, 128:256] = 0                       # an all-zero e4m3 block
+    (c, s, r, f), _ = assert_layout_equal(ids, e, align)
+    cap = oracle.capacity(bs, k, e, align)
+    got, ref, gflags, rflags = run_dispatch_bf16(ids, x, e, align)
+    assert gflags == rflags == 0
+    np.testing.assert_array_equal(got, ref)
+    gc, gs, rc, rs = run_dispatch_fp8(ids, x, e, align)
+    np.testing.assert_array_equal(gc, rc)
+    np.testing.assert_array_equal(gs.view(np.uint32), rs.view(np.uint32))
+    y = random_bf16(rng, (cap, h))
+    sc = workloads.scales(bs, k, seed=7)
+    sh = random_bf16(rng, (bs, h))
+    got, ref = run_combine(ids, y, sc, sh, e, align)
+    np.testing.assert_array_equal(got, ref)
+    got, ref = run_combine_fp8(ids, rc, rs, sc, sh, e, align)
+    np.testing.assert_array_equal(got, ref)
+    moe = moe_mod()
+    lay, ex = moe.moe_dispatch_fused(bf16_dev(x), dev(ids), e, align, capacity_rows=cap)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(lay.expand_idx.cpu().numpy(), r)
+    assert cap == bs * k                    # align 1: every row is a real row
+    np.testing.assert_array_equal(host_bits(ex), oracle.dispatch_bf16(x, ids, r, s, e, cap)[0])
