@@ -56,7 +56,8 @@ def parse():
                    help="split the N most popular experts into 4 replicas each and use the "
                         "replica-aware layout (probabilistic replica choice + count gathering)")
     p.add_argument("--sets", type=int, default=0,
-                   help="buffer sets rotated across steps (0 = enough to exceed 2 GiB)")
+                   help="buffer sets rotated across steps (0 = enough that no input stays "
+                        "cache-resident between uses; see buffer_sets)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
     p.add_argument("--fused", action="store_true",
@@ -177,6 +178,31 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
 
 
+MALL_BYTES = 256 << 20      # MI355X Infinity Cache
+SET_MEMORY_CAP = 48 << 30   # device memory the rotated buffer sets may take
+
+
+def buffer_sets(w, cap, step_bytes, fp8_combine):
+    """Buffer sets rotated across steps so that no input is served from a
+    cache between its uses.  The streaming kernels read expert rows and the
+    shared row with non-temporal loads and write with non-temporal stores,
+    which do not allocate in the 256 MB Infinity Cache; the token rows x are
+    read with ordinary loads and would stay resident across steps if few
+    sets cycled.  So: enough sets that the other sets' x (the allocating
+    traffic between two reads of one set's x) is at least twice the
+    Infinity Cache, and a whole cycle moves at least 2 GiB; capped by
+    SET_MEMORY_CAP of buffers and 64 sets.  At decode size the cap binds (each set holds
+    full-capacity expert buffers for 1.8 MB of token rows), as its note in
+    the output says."""
+    x_bytes = 2 * w.bs * w.hidden
+    per_set = (x_bytes * 3                                     # x, shared, out
+               + cap * w.hidden * (1 if w.fp8 else 2)          # expand_x
+               + cap * w.hidden * (1 if fp8_combine else 2))   # y (codes)
+    by_cache = 1 + -(-2 * MALL_BYTES // x_bytes)
+    by_volume = -(-(2 << 30) // step_bytes)
+    return max(1, min(max(by_cache, by_volume), SET_MEMORY_CAP // per_set, 64))
+
+
 def practical_ceiling(moe, w, launches=20):
     """GB/s of the plain streaming probe with the dispatch's 1 : K and the
     combine's (K + 1) : 1 row mixes at this workload's bf16 row size and
@@ -262,7 +288,7 @@ def main():
     nbytes = algorithmic_bytes(w.bs, w.hidden, n_phys, w.topk, inp["shared"] is not None,
                                fp8=w.fp8, fp8_combine=fp8_combine)
     step_bytes = sum(nbytes.values())
-    sets = args.sets or max(1, min(64, -(-(2 << 30) // step_bytes)))
+    sets = args.sets or buffer_sets(w, cap, step_bytes, fp8_combine)
 
     ids = torch.from_numpy(inp["expert_ids"]).to(dev)
     scales = torch.from_numpy(inp["expert_scales"]).to(dev)
@@ -444,6 +470,7 @@ def main():
                    "topk": w.topk, "routing": w.routing + (f"(alpha={w.alpha})"
                                                            if w.routing == "zipf" else ""),
                    "align": w.align, "capacity_rows": cap, "buffer_sets": sets,
+                   "x_bytes_between_reuse": 2 * w.bs * w.hidden * (sets - 1),
                    "launch": (f"hip graphs of {EVENT_EVERY} steps" if args.graph else "eager"),
                    "layout_dispatch": "moe_dispatch_fused" if args.fused else "separate",
                    "combine_input": "e4m3 + fp32 scales" if fp8_combine else "bf16",
