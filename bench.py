@@ -499,7 +499,9 @@ def main():
                      "traffic_unit": "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
                      "algorithmic_bytes_per_launch": nbytes["combine"]},
     }
-    if not (args.no_ceiling or w.fp8 or fp8_combine):   # the probe models bf16 rows
+    # The probe models bf16 rows at bandwidth-bound sizes (a decode-sized
+    # step is launch-latency bound, and a probe of it says nothing).
+    if not (args.no_ceiling or w.fp8 or fp8_combine or step_bytes < MALL_BYTES):
         ceil = practical_ceiling(moe, w)
         result["practical_ceiling"] = {
             "probe": "moe_probe_stream_mix: plain 16-B streaming kernel, same read:write row mix",
