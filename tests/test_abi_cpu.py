@@ -233,3 +233,21 @@ def test_probe_rules(lib):
     assert call(src_total=3) == 1                  # contiguous reads overrun src
     assert call(src=FAKE + 8) == 1                 # misaligned
     assert call(items=0, src=None, dst=None) == 0  # nothing to do
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No CPU fallback: with the library absent, loading it raises (in a
+    fresh interpreter whose library path points at an empty folder)."""
+    code = (
+        "import combine_moe_dispatch_layout_amd as m, os\n"
+        f"m._LIB_PATH = os.path.join({str(tmp_path)!r}, 'libmoe_dispatch.so')\n"
+        "m._lib = None\n"
+        "try:\n"
+        "    m.load_library()\n"
+        "except ImportError as e:\n"
+        "    print('raised:', e)\n"
+        "else:\n"
+        "    print('loaded')\n")
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT,
+                         timeout=120)
+    assert "raised:" in out.stdout and "no CPU fallback" in out.stdout, out.stdout + out.stderr
