@@ -8,8 +8,8 @@ chunk-migration planner with expert-affinity batching, a makespan guard, a
 cost-aware no-op and 128-aligned chunks, and reports ~99 % of the ideal bound;
 the TEMPO summary (section 2) gives the tile-aware cost model: an expert's
 time on a device is an activation floor plus a cost per 128-row M-tile.  The
-pages give no algorithm listing, so the steps below are this build's reading,
-written plainly; the library's C++ planner must reproduce them exactly.
+pages give no algorithm listing, so the steps below are one plain reading of
+those features; the library's C++ planner must reproduce them exactly.
 
 Model (integer cost units, so both implementations agree exactly):
   ranks r = 0..ws-1; expert e lives on rank e // L (L = E / ws);
