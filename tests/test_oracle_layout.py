@@ -191,3 +191,31 @@ def test_equal_out_of_range_ids_are_not_a_repeated_expert():
     c, send, r, flags = oracle.layout(ids, 4, 1)
     assert flags == oracle.FLAG_ID_RANGE
     np.testing.assert_array_equal(r, [-1, -1, -1, -1, 0, 0])
+
+
+def test_random_bad_and_repeated_ids_against_argsort():
+    """Out-of-range ids are dropped (rank -1, not counted) and repeats are
+    ranked in row-major order like distinct pairs: the argsort formulation
+    restricted to the valid pairs gives the same layout, and the flags are
+    set exactly when such ids occur."""
+    rng = np.random.default_rng(17)
+    for trial in range(120):
+        num_experts = int(rng.integers(1, 65))
+        k = int(rng.integers(1, min(num_experts, 16) + 1))
+        bs = int(rng.integers(0, 120))
+        ids = rng.integers(0, num_experts, size=(bs, k)).astype(np.int32)   # repeats likely
+        bad = rng.random(ids.shape) < (0.1 if trial % 2 else 0.0)
+        ids[bad] = rng.choice([-1, num_experts, num_experts + 3, -50], size=int(bad.sum()))
+        c, s, r, f = oracle.layout(ids, num_experts, 128)
+        flat = ids.ravel()
+        valid = (flat >= 0) & (flat < num_experts)
+        c2, s2, r2 = layout_by_argsort(flat[valid].reshape(-1, 1) if valid.any()
+                                       else np.zeros((0, 1), np.int32), num_experts, 128)
+        np.testing.assert_array_equal(c, c2)
+        np.testing.assert_array_equal(s, s2)
+        np.testing.assert_array_equal(r[valid], r2)
+        assert np.all(r[~valid] == -1)
+        rows_repeat = any(len(set(v for v in row if 0 <= v < num_experts)) <
+                          sum(1 for v in row if 0 <= v < num_experts) for row in ids)
+        assert bool(f & oracle.FLAG_ID_RANGE) == bool((~valid).any())
+        assert bool(f & oracle.FLAG_DUP_ID) == rows_repeat
