@@ -257,15 +257,41 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
     r[s] = (i < end) ? expand_idx[i] : -1;
     e[s] = (i < end) ? ids[i] : 0;
   }
-  // Column sums over the earlier workgroups' histograms; the loads of one
-  // batch of rows are independent, so they are issued together.
+  const int mine = (last && tid < E) ? block_hist[b * E + tid] : 0;
+  // Column sums over the earlier workgroups' histograms.  When E leaves
+  // threads over, `groups` threads share a column (E rounded up to a power
+  // of two, at most 16 per column), each summing every groups-th row, so one
+  // thread's chain of load batches is groups times shorter; the partial
+  // sums meet in LDS.
+  __shared__ int part[kLayoutThreads];
+  int epad = 1;
+  while (epad < E) epad <<= 1;
+  const int groups = min(16, kLayoutThreads / epad);  // workgroup-uniform
   int own = 0;
-  if (tid < E) {
-    int sum = 0;
+  if (groups == 1) {  // one thread per column: sum directly
+    if (tid < E) {
+      int sum = 0;
 #pragma unroll 8
-    for (int bb = 0; bb < b; ++bb) sum += block_hist[bb * E + tid];
-    base[tid] = sum;
-    if (last) own = sum + block_hist[b * E + tid];
+      for (int bb = 0; bb < b; ++bb) sum += block_hist[bb * E + tid];
+      base[tid] = sum;
+      own = sum + mine;
+    }
+  } else {
+    const int col = tid & (epad - 1);
+    const int grp = tid / epad;
+    int sum = 0;
+    if (col < E && grp < groups) {
+#pragma unroll 8
+      for (int bb = grp; bb < b; bb += groups) sum += block_hist[bb * E + col];
+    }
+    part[tid] = sum;
+    __syncthreads();
+    if (tid < E) {
+      int total = 0;
+      for (int g = 0; g < groups; ++g) total += part[g * epad + tid];
+      base[tid] = total;
+      own = total + mine;
+    }
   }
   if (last) {  // workgroup-uniform
     write_counts_and_offsets(own, E, align, wave_tot, counts, send, ranks);
