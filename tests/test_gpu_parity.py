@@ -632,3 +632,12 @@ def test_maximum_dimensions():
     np.testing.assert_array_equal(lay.expand_idx.cpu().numpy(), r)
     assert cap == bs * k                    # align 1: every row is a real row
     np.testing.assert_array_equal(host_bits(ex), oracle.dispatch_bf16(x, ids, r, s, e, cap)[0])
+
+
+def test_layout_many_workgroups_every_expert_count():
+    """Hundreds of ranking workgroups with E from 1 to 512, so the finalize
+    pass's column sums run with 16, 8, 4, 2 and 1 threads per column."""
+    rng = np.random.default_rng(103)
+    for bs, e, k in [(200000, 1, 1), (60000, 3, 2), (100000, 8, 2), (30000, 100, 8),
+                     (40000, 300, 4), (30000, 512, 16)]:
+        assert_layout_equal(random_ids(rng, bs, e, k), e, 128)
