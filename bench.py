@@ -465,6 +465,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16 (dispatch e4m3, fp32 scales)" if w.fp8 else "bf16",
+        "arithmetic": ("int32 layout; "
+                       + ("e4m3 quantisation in fp32" if w.fp8 else "bf16 bit copies")
+                       + " in dispatch; fp32 fused multiply-add chain in combine, "
+                         "rounded once to bf16"),
         "data": "synthetic (seeded generators; no routing trace or trained weights)",
         "config": {"workload": w.name, "bs": w.bs, "hidden": w.hidden, "experts": w.experts,
                    "topk": w.topk, "routing": w.routing + (f"(alpha={w.alpha})"
