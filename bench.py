@@ -1,24 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE dispatch -> combine hot path on one MI355X.
 
-One step = the whole path on one batch: moe_dispatch_layout (counts, padded
-prefix, stable ranks) -> moe_dispatch (bf16 scatter into the
-expert-contiguous, 128-row-padded buffer) -> moe_combine (weighted gather-sum
-+ shared row).  Inputs are seeded synthetic tensors already resident in HBM
-when the timed region starts.  Prints ONE JSON line.
+One step = the whole path on one batch: counts, padded prefix and stable
+ranks, the bf16 scatter into the expert-contiguous, 128-row-padded buffer
+(moe_dispatch_fused: layout and scatter in one call), then moe_combine
+(weighted gather-sum + shared row).  Inputs are seeded synthetic tensors
+already resident in HBM when the timed region starts.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload skewed] [--graph] [--fused]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload skewed]
+                    [--separate] [--graph]
 
 `value` is algorithmic bytes per step (real rows only, never padding) divided
 by the measured step time, in GB/s; `tokens_per_s` is tokens per step over the
 same time.  The `roofline` object covers the kernel that moves the most bytes
 (combine): its algorithmic bytes per launch over its mean launch time measured
 with HIP events on the launch stream around the combine of every 10th step
-inside the timed region.  `--graph` replays the steps as captured HIP graphs
-of 10 steps each (split before the combine that the events bracket) instead
-of eager launches; `--fused` runs layout + dispatch through moe_dispatch_fused
-(one launch for batches of at most 2048 pairs).  `cpu_baseline`
-times the CPU oracle (single-threaded C) on the same workload.
+inside the timed region.  `--separate` runs layout and dispatch as two calls
+(moe_dispatch_layout, moe_dispatch); `--graph` replays the steps as captured
+HIP graphs of 10 steps each (split before the combine that the events
+bracket) instead of eager launches.  `cpu_baseline` times the CPU oracle on
+the same workload.
 """
 
 from __future__ import annotations
@@ -60,9 +61,13 @@ def parse():
                         "cache-resident between uses; see buffer_sets)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
+    p.add_argument("--separate", action="store_true",
+                   help="layout and dispatch as two calls (moe_dispatch_layout, moe_dispatch) "
+                        "instead of moe_dispatch_fused")
     p.add_argument("--fused", action="store_true",
-                   help="layout + dispatch through moe_dispatch_fused (one launch for "
-                        "batches of at most 2048 pairs)")
+                   help="layout + dispatch through moe_dispatch_fused (the default; one launch "
+                        "for batches of at most 2048 pairs, else the layout launches read the "
+                        "token rows ahead for the scatter)")
     p.add_argument("--graph", action="store_true",
                    help="replay the steps as captured HIP graphs of 10 steps instead of eager "
                         "launches")
@@ -254,10 +259,13 @@ def main():
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               "(the path is single-device; no collectives are built)", file=sys.stderr)
         sys.exit(2)
-    if args.fused and args.replicas > 0:
-        print("--fused takes logical expert ids; it does not combine with --replicas",
-              file=sys.stderr)
+    if args.fused and (args.separate or args.replicas > 0):
+        print("--fused takes logical expert ids; it does not combine with --separate or "
+              "--replicas", file=sys.stderr)
         sys.exit(2)
+    # moe_dispatch_fused is the step's layout + dispatch unless asked otherwise
+    # (the replica-aware layout has no fused form).
+    args.fused = not (args.separate or args.replicas > 0)
     import torch
     if args.copy_probe:
         copy_probe()

@@ -221,9 +221,18 @@ int moe_dispatch_fused(const void* x, int64_t x_stride, int32_t bs, int32_t hidd
   const size_t need = moe::layout_workspace_bytes(plan, num_experts);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return MOE_ERR_WORKSPACE;
+  // The layout launches read the token rows ahead for the scatter (x must be
+  // contiguous: the read-ahead walks one range).
+  moe::ReadAhead ahead;
+  if (bs > 0 && x_stride == hidden) {
+    const int64_t vecs = (int64_t)bs * hidden / 8;
+    const int64_t max_vecs = moe::kReadAheadMaxBytes / 16;
+    ahead.base = static_cast<const moe::u32x4*>(x);
+    ahead.vecs = vecs < max_vecs ? vecs : max_vecs;
+  }
   hipError_t err = moe::launch_layout(expert_ids, k, num_experts, align, plan, expert_counts,
                                       ep_send_counts, expand_idx, status, workspace,
-                                      moe::ReplicaMap{}, moe::RankSplit{}, s);
+                                      moe::ReplicaMap{}, moe::RankSplit{}, s, ahead);
   if (err != hipSuccess || bs == 0) return hip_status(err);
   if (out_dtype == MOE_BF16)
     return hip_status(moe::launch_dispatch_bf16(x, x_stride, bs, hidden, expert_ids, expand_idx,

@@ -67,7 +67,8 @@ __device__ void write_counts_and_offsets(int c, int32_t E, int32_t align, int* w
   if (e < E) {
     counts[e] = c;
     send[e] = excl;
-    if (ranks.offsets != nullptr && e % ranks.per_rank == 0) ranks.offsets[e / ranks.per_rank] = excl;
+    if (ranks.offsets != nullptr && e % ranks.per_rank == 0)
+      ranks.offsets[e / ranks.per_rank] = excl;
   }
   if (e == 0) {
     send[E] = total;
@@ -77,8 +78,8 @@ __device__ void write_counts_and_offsets(int c, int32_t E, int32_t align, int* w
 
 // Flags an expert (an id in [0, E)) repeated within one of the tokens whose
 // first pair lies in [begin, end).
-__device__ __forceinline__ int duplicate_flags(const int32_t* __restrict__ ids, int32_t k, int32_t E, int begin,
-                               int end) {
+__device__ __forceinline__ int duplicate_flags(const int32_t* __restrict__ ids, int32_t k,
+                                               int32_t E, int begin, int end) {
   int fl = 0;
   for (int t = (begin + k - 1) / k + (int)threadIdx.x; t * k < end; t += kLayoutThreads) {
     int v[kMaxTopK];
@@ -114,7 +115,12 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     const int32_t* __restrict__ ids, int32_t n_pairs, int32_t k, int32_t E, int32_t align,
     int32_t* __restrict__ expand_idx, int32_t* __restrict__ block_hist,
     int32_t* __restrict__ block_flags, int32_t* __restrict__ counts, int32_t* __restrict__ send,
-    int32_t* __restrict__ status, ReplicaMap map, RankSplit ranks) {
+    int32_t* __restrict__ status, ReplicaMap map, RankSplit ranks, ReadAhead ahead,
+    int32_t rank_blocks, int32_t ahead_blocks) {
+  if ((int32_t)blockIdx.x >= rank_blocks) {  // read-ahead workgroup: first half
+    read_ahead(ahead, rank_blocks, ahead_blocks, 0, ahead.vecs / 2);
+    return;
+  }
   __shared__ unsigned long long mask[kLayoutWaves][kMaxExperts];  // 32 KB
   __shared__ int wave_run[kLayoutWaves][kMaxExperts];             // 16 KB
   __shared__ int rep_off[kMaxExperts + 1];
@@ -236,7 +242,11 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
     int32_t pairs_per_block, int32_t nblocks, const int32_t* __restrict__ block_hist,
     const int32_t* __restrict__ block_flags, int32_t* __restrict__ expand_idx,
     int32_t* __restrict__ counts, int32_t* __restrict__ send, int32_t* __restrict__ status,
-    RankSplit ranks) {
+    RankSplit ranks, ReadAhead ahead, int32_t ahead_blocks) {
+  if ((int32_t)blockIdx.x >= nblocks) {  // read-ahead workgroup: second half
+    read_ahead(ahead, nblocks, ahead_blocks, ahead.vecs / 2, ahead.vecs);
+    return;
+  }
   __shared__ int base[kMaxExperts];
   __shared__ int wave_tot[kLayoutWaves];
   const int b = blockIdx.x;
@@ -342,10 +352,10 @@ template <int R>
 void launch_rank(const LayoutPlan& plan, const int32_t* ids, int32_t k, int32_t E, int32_t align,
                  int32_t* expand_idx, int32_t* hist, int32_t* bflags, int32_t* counts,
                  int32_t* send, int32_t* status, const ReplicaMap& map, const RankSplit& ranks,
-                 hipStream_t stream) {
-  layout_rank_kernel<R><<<plan.blocks, kLayoutThreads, 0, stream>>>(
+                 hipStream_t stream, const ReadAhead& ahead, int32_t ahead_blocks) {
+  layout_rank_kernel<R><<<plan.blocks + ahead_blocks, kLayoutThreads, 0, stream>>>(
       ids, (int32_t)plan.n_pairs, k, E, align, expand_idx, hist, bflags, counts, send, status,
-      map, ranks);
+      map, ranks, ahead, plan.blocks, ahead_blocks);
 }
 
 }  // namespace
@@ -353,7 +363,14 @@ void launch_rank(const LayoutPlan& plan, const int32_t* ids, int32_t k, int32_t 
 hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int32_t align,
                          const LayoutPlan& plan, int32_t* counts, int32_t* send,
                          int32_t* expand_idx, int32_t* status, void* workspace,
-                         const ReplicaMap& map, const RankSplit& ranks, hipStream_t stream) {
+                         const ReplicaMap& map, const RankSplit& ranks, hipStream_t stream,
+                         const ReadAhead& ahead) {
+  // Read-ahead workgroups only ride along the two-launch layout, and only
+  // while the ranking workgroups leave compute units free.
+  const int32_t ahead_blocks =
+      (plan.blocks > 1 && ahead.vecs > 0 && plan.blocks < kReadAheadMaxBlocks)
+          ? kReadAheadMaxBlocks - plan.blocks
+          : 0;
   int32_t* hist = nullptr;
   int32_t* bflags = nullptr;
   if (plan.blocks > 1) {
@@ -364,23 +381,23 @@ hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int
   }
   switch (plan.rounds) {
     case 1: launch_rank<1>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, map, ranks, stream); break;
+                           send, status, map, ranks, stream, ahead, ahead_blocks); break;
     case 2: launch_rank<2>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, map, ranks, stream); break;
+                           send, status, map, ranks, stream, ahead, ahead_blocks); break;
     case 4: launch_rank<4>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, map, ranks, stream); break;
+                           send, status, map, ranks, stream, ahead, ahead_blocks); break;
     case 8: launch_rank<8>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, map, ranks, stream); break;
+                           send, status, map, ranks, stream, ahead, ahead_blocks); break;
     default: launch_rank<16>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                             send, status, map, ranks, stream); break;
+                             send, status, map, ranks, stream, ahead, ahead_blocks); break;
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.blocks <= 1) return err;
   // The finalize pass looks pairs up by the id they were ranked under.
   const int32_t* ranked_ids = map.offsets != nullptr ? map.out : ids;
-  layout_finalize_kernel<<<plan.blocks, kLayoutThreads, 0, stream>>>(
+  layout_finalize_kernel<<<plan.blocks + ahead_blocks, kLayoutThreads, 0, stream>>>(
       ranked_ids, (int32_t)plan.n_pairs, num_experts, align, (int32_t)plan.pairs_per_block,
-      plan.blocks, hist, bflags, expand_idx, counts, send, status, ranks);
+      plan.blocks, hist, bflags, expand_idx, counts, send, status, ranks, ahead, ahead_blocks);
   return hipGetLastError();
 }
 

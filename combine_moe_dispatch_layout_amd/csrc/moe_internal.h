@@ -21,7 +21,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // bf16 held in the low / high half of a 32-bit word -> fp32 (exact).
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) {
+  return __uint_as_float(w & 0xFFFF0000u);
+}
 
 // fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -209,13 +211,51 @@ struct RankSplit {
   int32_t ranks = 0;
 };
 
+// Token rows that the layout launches read ahead.  The layout is latency
+// bound and leaves HBM nearly idle, so up to kReadAheadMaxBlocks workgroups
+// of each of its two launches (together with the ranking workgroups) read
+// the rows the scatter will need with ordinary loads, which allocate in the
+// 256 MB Infinity Cache; the scatter then finds them there instead of
+// mixing row reads from HBM into its write stream.  At most
+// kReadAheadMaxBytes are read ahead (half the cache).
+struct ReadAhead {
+  const u32x4* base = nullptr;
+  int64_t vecs = 0;  // 16-byte vectors, from base
+};
+constexpr int kReadAheadMaxBlocks = 240;  // of the 256 compute units, with the ranking workgroups
+constexpr int64_t kReadAheadMaxBytes = int64_t(128) << 20;
+constexpr int kReadAheadUnroll = 16;      // loads in flight per thread
+
+// Body of a read-ahead workgroup: block `blockIdx.x - first_block` of
+// `blocks` reads its share of vectors [lo, hi).  Nothing is stored; the
+// empty asm statement consumes the loaded values so the loads are kept.
+__device__ __forceinline__ void read_ahead(const ReadAhead& ra, int32_t first_block,
+                                           int32_t blocks, int64_t lo, int64_t hi) {
+  const int64_t per = (hi - lo + blocks - 1) / blocks;
+  const int64_t s = lo + ((int64_t)blockIdx.x - first_block) * per;
+  const int64_t e = s + per < hi ? s + per : hi;
+  uint32_t acc = 0;
+  for (int64_t v0 = s; v0 < e; v0 += (int64_t)blockDim.x * kReadAheadUnroll) {
+    u32x4 t[kReadAheadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadAheadUnroll; ++u) {
+      const int64_t v = v0 + (int64_t)u * blockDim.x + threadIdx.x;
+      t[u] = (v < e) ? ra.base[v] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kReadAheadUnroll; ++u) acc ^= t[u][0] ^ t[u][1] ^ t[u][2] ^ t[u][3];
+  }
+  __asm__ volatile("" : : "v"(acc));
+}
+
 LayoutPlan plan_layout(int32_t bs, int32_t k);
 size_t layout_workspace_bytes(const LayoutPlan& p, int32_t num_experts);
 
 hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int32_t align,
                          const LayoutPlan& plan, int32_t* counts, int32_t* send,
                          int32_t* expand_idx, int32_t* status, void* workspace,
-                         const ReplicaMap& map, const RankSplit& ranks, hipStream_t stream);
+                         const ReplicaMap& map, const RankSplit& ranks, hipStream_t stream,
+                         const ReadAhead& ahead = ReadAhead{});
 
 // Batches of at most this many pairs fit one layout workgroup; the fused
 // layout + bf16 scatter derives the layout in every scatter workgroup.

@@ -234,7 +234,11 @@ int moe_dispatch(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
  * so no separate layout launch or wait precedes the scatter (the TEMPO
  * summary, section 2, folds count gathering into the dispatch kernel; here
  * the counts, offsets and ranks are folded in).  Larger batches run the
- * layout and dispatch kernels in sequence.
+ * layout and dispatch kernels in sequence; the layout launches, which are
+ * latency bound, then also read the token rows x ahead (ordinary loads, at
+ * most 128 MB, x contiguous) so that the scatter finds them in the 256 MB
+ * Infinity Cache instead of interleaving row reads from HBM with its
+ * writes.  HBM still reads x once.
  *
  *  x, x_stride, bs, hidden                   as for moe_dispatch.
  *  expert_ids, k, num_experts, align         as for moe_dispatch_layout.
