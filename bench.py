@@ -13,13 +13,17 @@ already resident in HBM when the timed region starts.  Prints ONE JSON line.
 `value` is algorithmic bytes per step (real rows only, never padding) divided
 by the measured step time, in GB/s; `tokens_per_s` is tokens per step over the
 same time.  The `roofline` object covers the kernel that moves the most bytes
-(combine): its algorithmic bytes per launch over its mean launch time measured
-with HIP events on the launch stream around the combine of every 10th step
-inside the timed region.  `--separate` runs layout and dispatch as two calls
-(moe_dispatch_layout, moe_dispatch); `--graph` replays the steps as captured
-HIP graphs of 10 steps each (split before the combine that the events
-bracket) instead of eager launches.  `cpu_baseline` times the CPU oracle on
-the same workload.
+(combine): its algorithmic bytes per launch over its mean kernel time, from
+HIP events bound to the combine launch of every 10th step inside the timed
+region (moe_time_next_launches: the runtime stamps them with the kernel's own
+start and end on the launch stream).  `kernels_ms` adds the layout and
+dispatch kernels, timed the same way in 10 steps after the timed region.
+
+`--separate` runs layout and dispatch as two calls (moe_dispatch_layout,
+moe_dispatch); `--graph` replays the steps as captured HIP graphs of 10 steps
+each, split before the last combine, which events recorded around its
+replay time instead.  `cpu_baseline` times the CPU oracle on the same
+workload.
 """
 
 from __future__ import annotations
@@ -37,7 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
-EVENT_EVERY = 10        # combine launches bracketed by events: every 10th step
+EVENT_EVERY = 10        # one combine timed by events every 10 steps
 METRIC = "dispatch+combine achieved HBM GB/s and tokens/s, H=7168 E=256 K=8 bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_bf16_skewed_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_moe_dispatch_layout_amd", "csrc", f)
@@ -208,13 +212,13 @@ def buffer_sets(w, cap, step_bytes, fp8_combine):
     return max(1, min(max(by_cache, by_volume), SET_MEMORY_CAP // per_set, 64))
 
 
-def practical_ceiling(moe, w, launches=20):
+def practical_ceiling(moe, w, launches=16):
     """GB/s of the plain streaming probe with the dispatch's 1 : K and the
     combine's (K + 1) : 1 row mixes at this workload's bf16 row size and
     token count: all rows in order, and with the K expert-side rows randomly
     permuted as the real layout scatters them (seeded; the token-side rows
-    stay in order).  Mean over `launches` launches bracketed by HIP events,
-    after 3 warm-up launches."""
+    stay in order).  Mean kernel time of `launches` launches (at most 16),
+    each timed by HIP events bound to it, after 3 warm-up launches."""
     import numpy as np
     import torch
     bs, k, row_bytes = w.bs, w.topk, 2 * w.hidden
@@ -239,13 +243,16 @@ def practical_ceiling(moe, w, launches=20):
                                                    dst_rows)
             for _ in range(3):
                 run()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(launches)]
+            for a, z in pairs:
+                a.record()
+                z.record()
+            moe.moe_time_next_launches(pairs)
             for _ in range(launches):
                 run()
-            e1.record()
             torch.cuda.synchronize()
-            secs = e0.elapsed_time(e1) / 1e3 / launches
+            secs = sum(a.elapsed_time(z) for a, z in pairs) / 1e3 / launches
             res[order] = round(bs * (reads + writes) * row_bytes / secs / 1e9, 1)
         out[name] = res
         del src, dst
@@ -363,13 +370,46 @@ def main():
         dispatch(b, lay)
         return lay
 
-    def step(b, ev=None):
+    def step(b, pair=None):
+        """One step.  With `pair`, the combine launch takes that (start,
+        stop) event pair, stamped with the kernel's own start and end
+        (moe_time_next_launches)."""
         lay = front(b)
-        if ev is not None:
-            ev[0].record(stream)
+        if pair is not None:
+            moe.moe_time_next_launches([pair])
         combine(b, lay)
-        if ev is not None:
-            ev[1].record(stream)
+        if pair is not None and moe.moe_time_unused_launches():
+            raise SystemExit("the combine launched no kernel")
+
+    def breakdown_step(b, pairs):
+        """One step with every kernel launch taking one of `pairs`; returns
+        the pairs taken, in launch order (the combine last)."""
+        moe.moe_time_next_launches(pairs)
+        combine(b, front(b))
+        used = len(pairs) - moe.moe_time_unused_launches()
+        moe.moe_time_next_launches([])
+        return pairs[:used]
+
+    def new_pairs(n):
+        """n (start, stop) timing-event pairs, each recorded once so that the
+        event exists before a launch is bound to it."""
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(n)]
+        for a, z in pairs:
+            a.record(stream)
+            z.record(stream)
+        return pairs
+
+    def split_kernels(taken):
+        """Kernel times (ms) of one step by role: the combine is the last
+        launch, the dispatch the one before it, the layout's one or two
+        launches come first; moe_dispatch_fused's single-launch form is one
+        fused kernel."""
+        ms = [a.elapsed_time(z) for a, z in taken]
+        if len(ms) == 2:
+            return {"layout+dispatch (fused)": ms[0], "combine": ms[1]}
+        return {"layout": sum(ms[:-2]), "dispatch": ms[-2], "combine": ms[-1],
+                "layout_launches": len(ms) - 2}
 
     for i in range(args.warmup):
         step(bufs[i % sets])
@@ -404,47 +444,39 @@ def main():
             back.replay()
         torch.cuda.synchronize()
 
-    # Timed region: K steps on the host clock.  HIP events on the launch stream
-    # bracket the combine launch of every EVENT_EVERY-th step (each event
-    # record costs a few microseconds on this runtime, so not every step).
-    events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-              for i in range(0, args.steps, EVENT_EVERY)}
+    # Timed region: K steps on the host clock.  Eager: the combine launch of
+    # every EVENT_EVERY-th step takes HIP events bound to it, which the
+    # runtime stamps with the kernel's own start and end on the launch
+    # stream.  A bound launch adds ~5 us to its step, so not every
+    # step is timed, and the layout and dispatch launches are timed after the
+    # timed region.  Graph replays cannot carry bound events, so there events
+    # recorded on the stream bracket the replay of the graph that holds one
+    # combine launch; they also hold that replay's launch gap.
+    pairs = {i: new_pairs(1)[0] for i in range(0, args.steps, EVENT_EVERY)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if graphs is None:
         for i in range(args.steps):
-            step(bufs[i % sets], events.get(i))
+            step(bufs[i % sets], pairs.get(i))
     else:
         for c in range(args.steps // EVENT_EVERY):
             head, back = graphs[c % len(graphs)]
-            ev = events[c * EVENT_EVERY]
+            ev0, ev1 = pairs[c * EVENT_EVERY]
             head.replay()
-            ev[0].record(stream)
+            ev0.record(stream)
             back.replay()
-            ev[1].record(stream)
+            ev1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    com_ms = [e[0].elapsed_time(e[1]) for e in events.values()]
+    com_ms = [ev0.elapsed_time(ev1) for ev0, ev1 in pairs.values()]
 
-    # Per-kernel breakdown (outside the timed region: event records between
-    # kernels cost a few microseconds each on this runtime).
-    brk = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(10)]
-    for i, e in enumerate(brk):
-        b = bufs[i % sets]
-        e[0].record(stream)
-        if args.fused:
-            lay = front(b)
-            e[1].record(stream)
-        else:
-            lay = layout(b)
-            e[1].record(stream)
-            dispatch(b, lay)
-        e[2].record(stream)
-        combine(b, lay)
-        e[3].record(stream)
+    # Per-kernel split: 10 eager steps after the timed region, every launch
+    # timed by its own bound events.
+    steps_taken = [breakdown_step(bufs[i % sets], new_pairs(16)) for i in range(10)]
     torch.cuda.synchronize()
-    lay_ms = [e[0].elapsed_time(e[1]) for e in brk]
-    dis_ms = [e[1].elapsed_time(e[2]) for e in brk]
+    per_step = [split_kernels(t) for t in steps_taken]
+    kern_ms = {r: [d[r] for d in per_step] for r in per_step[0] if r != "layout_launches"}
+    kern_ms["combine"] = com_ms
     mean = lambda v: sum(v) / len(v)
 
     def pct(v):
@@ -458,6 +490,9 @@ def main():
         raise SystemExit(f"layout status flags {status}: routing is invalid")
 
     combine_s = mean(com_ms) / 1e3
+    role_bytes = {"layout": nbytes["layout"], "dispatch": nbytes["dispatch"],
+                  "combine": nbytes["combine"],
+                  "layout+dispatch (fused)": nbytes["layout"] + nbytes["dispatch"]}
     achieved = nbytes["combine"] / combine_s / 1e9
     traffic = None if (fp8_combine or args.replicas > 0) else read_traffic(w.name)
     result = {
@@ -489,22 +524,18 @@ def main():
                    "replicas": ({"hot_experts": args.replicas, "per_hot": 4,
                                  "physical": n_phys} if args.replicas > 0 else None),
                    "bytes_per_step": step_bytes},
-        "kernels_ms": ({"layout+dispatch (fused)": round(mean(lay_ms), 4),
-                        "combine": round(mean(com_ms), 4)} if args.fused else
-                       {"layout": round(mean(lay_ms), 4), "dispatch": round(mean(dis_ms), 4),
-                        "combine": round(mean(com_ms), 4)}),
-        "kernels_gbs": ({"layout+dispatch (fused)":
-                         round((nbytes["layout"] + nbytes["dispatch"]) / mean(lay_ms) / 1e6, 1),
-                         "combine": round(achieved, 1)} if args.fused else
-                        {"layout": round(nbytes["layout"] / mean(lay_ms) / 1e6, 1),
-                         "dispatch": round(nbytes["dispatch"] / mean(dis_ms) / 1e6, 1),
-                         "combine": round(achieved, 1)}),
-        "kernels_us_p10_p50_p90": ({"layout+dispatch (fused)": pct(lay_ms),
-                                    "combine": pct(com_ms)} if args.fused else
-                                   {"layout": pct(lay_ms), "dispatch": pct(dis_ms),
-                                    "combine": pct(com_ms)}),
+        "kernel_times": ("combine: timed region; layout and dispatch: 10 eager steps after "
+                         "it, events bound to each kernel launch"),
+        "layout_launches": per_step[0].get("layout_launches", 0),
+        "kernels_ms": {r: round(mean(v), 4) for r, v in kern_ms.items()},
+        "kernels_gbs": {r: round(role_bytes[r] / mean(v) / 1e6, 1) for r, v in kern_ms.items()},
+        "kernels_us_p10_p50_p90": {r: pct(v) for r, v in kern_ms.items()},
         "roofline": {"kernel": "combine_fp8" if fp8_combine else "combine", "bound": "hbm",
-                     "timed_launches": len(com_ms), "achieved": round(achieved, 1),
+                     "timed_launches": len(com_ms),
+                     "timing": ("HIP events on the launch stream around the graph replay "
+                                "holding the combine" if graphs is not None else
+                                "HIP events bound to the combine launch (kernel start to end)"),
+                     "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
@@ -521,7 +552,7 @@ def main():
             "combine_frac_of_random_rows": round(
                 achieved / ceil["combine_mix"]["random_rows"], 4),
             "dispatch_frac_of_random_rows": round(
-                nbytes["dispatch"] / (mean(dis_ms) / 1e3) / 1e9
+                nbytes["dispatch"] / (mean(kern_ms["dispatch"]) / 1e3) / 1e9
                 / ceil["dispatch_mix"]["random_rows"], 4) if not args.fused else None}
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

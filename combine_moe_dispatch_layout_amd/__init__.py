@@ -28,6 +28,9 @@ Entry points (same names as the C ABI):
 * ``moe_dispatch_capacity`` / ``moe_dispatch_layout_workspace_size``
 * ``moe_probe_stream_mix`` (measurement only: a plain streaming kernel with a
   chosen read : write row mix, for practical-ceiling figures)
+* ``moe_time_next_launches(pairs)`` / ``moe_time_unused_launches()``
+  (measurement only: torch events stamped with the next kernels' own start
+  and end)
 """
 
 from __future__ import annotations
@@ -45,7 +48,8 @@ __all__ = [
     "moe_dispatch_capacity", "moe_dispatch_layout_workspace_size",
     "moe_dispatch_layout", "moe_dispatch_layout_ep", "moe_dispatch_layout_replicated",
     "moe_dispatch", "moe_dispatch_fused", "moe_combine", "moe_plan_compensation",
-    "moe_combine_fp8", "moe_probe_stream_mix",
+    "moe_combine_fp8", "moe_probe_stream_mix", "moe_time_next_launches",
+    "moe_time_unused_launches",
     "MOE_BF16", "MOE_FP8_E4M3", "MOE_FLAG_ID_RANGE", "MOE_FLAG_DUP_ID", "MOE_FLAG_GUARD",
 ]
 
@@ -99,6 +103,8 @@ def load_library() -> ctypes.CDLL:
         "moe_dispatch_layout_ep": (ctypes.c_int, [P, i32, i32, i32, i32, i32, P, P, P, P, P, P,
                                                   sz, P]),
         "moe_probe_stream_mix": (ctypes.c_int, [P, i64, P, i64, i32, i32, i32, i32, P, P, P]),
+        "moe_time_next_launches": (ctypes.c_int, [P, P, i32]),
+        "moe_time_unused_launches": (i32, []),
         "moe_dispatch_layout_replicated": (ctypes.c_int, [P, i32, i32, i32, P, P, i32,
                                                           ctypes.c_uint64, i32, P, P, P, P, P, P,
                                                           sz, P]),
@@ -441,3 +447,29 @@ def moe_probe_stream_mix(src: torch.Tensor, dst: torch.Tensor, items: int, reads
         _ptr(src), src.shape[0], _ptr(dst), dst.shape[0], items, row_bytes, reads, writes,
         _ptr(src_rows), _ptr(dst_rows), _stream(src))
     _check(rc)
+
+
+def moe_time_next_launches(pairs) -> None:
+    """Binds the next len(pairs) kernel launches of this host thread to
+    (start, stop) torch.cuda.Event pairs created with enable_timing=True
+    (include/moe_probe.h): each event pair gets its kernel's own start and
+    end, and start.elapsed_time(stop) is that kernel's time.  An event must
+    have been recorded once so that it exists.  An empty list drops the
+    pairs still bound."""
+    pairs = list(pairs)
+    handles = []
+    for start, stop in pairs:
+        for ev in (start, stop):
+            if not isinstance(ev, torch.cuda.Event) or not ev.cuda_event:
+                raise ValueError("pairs must hold torch.cuda.Event objects recorded once")
+        handles.append((start.cuda_event, stop.cuda_event))
+    arr = (ctypes.c_void_p * max(len(pairs), 1))
+    starts = arr(*[h[0] for h in handles])
+    stops = arr(*[h[1] for h in handles])
+    _check(load_library().moe_time_next_launches(starts, stops, len(pairs)))
+
+
+def moe_time_unused_launches() -> int:
+    """Number of event pairs bound by moe_time_next_launches that no launch
+    has taken yet (this host thread)."""
+    return int(load_library().moe_time_unused_launches())

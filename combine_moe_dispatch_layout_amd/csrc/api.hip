@@ -15,6 +15,7 @@
 #include <stdint.h>
 
 #include "moe_internal.h"
+#include "moe_probe.h"
 
 
 namespace {
@@ -52,7 +53,31 @@ bool rows_fit(int32_t bs, int32_t hidden) { return (int64_t)bs * (hidden / 8) <=
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Event pairs bound by moe_time_next_launches, per host thread; pairs
+// [next, n) are still to be taken by launches.
+constexpr int kMaxTimedLaunches = 16;
+struct TimedLaunches {
+  hipEvent_t start[kMaxTimedLaunches];
+  hipEvent_t stop[kMaxTimedLaunches];
+  int n = 0;
+  int next = 0;
+};
+thread_local TimedLaunches tl_timed;
+
 }  // namespace
+
+namespace moe {
+
+bool take_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+  TimedLaunches& t = tl_timed;
+  if (t.next >= t.n) return false;
+  *start = t.start[t.next];
+  *stop = t.stop[t.next];
+  ++t.next;
+  return true;
+}
+
+}  // namespace moe
 
 extern "C" {
 
@@ -229,6 +254,7 @@ int moe_dispatch_fused(const void* x, int64_t x_stride, int32_t bs, int32_t hidd
     const int64_t max_vecs = moe::kReadAheadMaxBytes / 16;
     ahead.base = static_cast<const moe::u32x4*>(x);
     ahead.vecs = vecs < max_vecs ? vecs : max_vecs;
+    ahead.split = ahead.vecs * moe::kReadAheadRankPercent / 100;
   }
   hipError_t err = moe::launch_layout(expert_ids, k, num_experts, align, plan, expert_counts,
                                       ep_send_counts, expand_idx, status, workspace,
@@ -295,5 +321,22 @@ int moe_combine_fp8(const void* expand_x, int64_t expand_x_stride, int64_t capac
                                             shared_stride, bs, hidden, k, num_experts, x_out,
                                             status, static_cast<hipStream_t>(stream)));
 }
+
+int moe_time_next_launches(void* const* start_events, void* const* stop_events, int32_t n) {
+  if (n < 0 || n > kMaxTimedLaunches) return MOE_ERR_INVALID_ARG;
+  if (n > 0 && (start_events == nullptr || stop_events == nullptr)) return MOE_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    if (start_events[i] == nullptr || stop_events[i] == nullptr) return MOE_ERR_INVALID_ARG;
+  TimedLaunches& t = tl_timed;
+  for (int32_t i = 0; i < n; ++i) {
+    t.start[i] = static_cast<hipEvent_t>(start_events[i]);
+    t.stop[i] = static_cast<hipEvent_t>(stop_events[i]);
+  }
+  t.n = n;
+  t.next = 0;
+  return MOE_OK;
+}
+
+int32_t moe_time_unused_launches(void) { return tl_timed.n - tl_timed.next; }
 
 }  // extern "C"

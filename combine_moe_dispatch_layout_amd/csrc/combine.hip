@@ -176,22 +176,22 @@ hipError_t launch_t(int kmax, dim3 grid, const u32x4* y, int64_t ys, int64_t cap
                     int32_t* status, hipStream_t stream) {
   switch (kmax) {
     case 2:
-      combine_kernel<THREADS, VPT, 2><<<grid, THREADS, 0, stream>>>(
+      launch_kernel(combine_kernel<THREADS, VPT, 2>, grid, THREADS, stream,
           y, ys, cap, ids, idx, send, scales, shared, ss, nvec, nchunks, k, E, out,
           status);
       break;
     case 4:
-      combine_kernel<THREADS, VPT, 4><<<grid, THREADS, 0, stream>>>(
+      launch_kernel(combine_kernel<THREADS, VPT, 4>, grid, THREADS, stream,
           y, ys, cap, ids, idx, send, scales, shared, ss, nvec, nchunks, k, E, out,
           status);
       break;
     case 8:
-      combine_kernel<THREADS, VPT, 8><<<grid, THREADS, 0, stream>>>(
+      launch_kernel(combine_kernel<THREADS, VPT, 8>, grid, THREADS, stream,
           y, ys, cap, ids, idx, send, scales, shared, ss, nvec, nchunks, k, E, out,
           status);
       break;
     default:
-      combine_kernel<THREADS, VPT, 16><<<grid, THREADS, 0, stream>>>(
+      launch_kernel(combine_kernel<THREADS, VPT, 16>, grid, THREADS, stream,
           y, ys, cap, ids, idx, send, scales, shared, ss, nvec, nchunks, k, E, out,
           status);
       break;
@@ -242,22 +242,22 @@ hipError_t launch_combine_fp8(const void* y, int64_t y_stride, int64_t capacity_
   const int kmax = k <= 2 ? 2 : k <= 4 ? 4 : k <= 8 ? 8 : 16;
   switch (kmax) {
     case 2:
-      combine_fp8_kernel<2><<<grid, threads, 0, stream>>>(
+      launch_kernel(combine_fp8_kernel<2>, grid, threads, stream,
           yv, ys, y_scales, nblk, capacity_rows, ids, expand_idx, send, scales, sv, ss, ngroups,
           nchunks, k, num_experts, ov, status);
       break;
     case 4:
-      combine_fp8_kernel<4><<<grid, threads, 0, stream>>>(
+      launch_kernel(combine_fp8_kernel<4>, grid, threads, stream,
           yv, ys, y_scales, nblk, capacity_rows, ids, expand_idx, send, scales, sv, ss, ngroups,
           nchunks, k, num_experts, ov, status);
       break;
     case 8:
-      combine_fp8_kernel<8><<<grid, threads, 0, stream>>>(
+      launch_kernel(combine_fp8_kernel<8>, grid, threads, stream,
           yv, ys, y_scales, nblk, capacity_rows, ids, expand_idx, send, scales, sv, ss, ngroups,
           nchunks, k, num_experts, ov, status);
       break;
     default:
-      combine_fp8_kernel<16><<<grid, threads, 0, stream>>>(
+      launch_kernel(combine_fp8_kernel<16>, grid, threads, stream,
           yv, ys, y_scales, nblk, capacity_rows, ids, expand_idx, send, scales, sv, ss, ngroups,
           nchunks, k, num_experts, ov, status);
       break;

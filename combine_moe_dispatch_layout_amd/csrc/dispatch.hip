@@ -117,22 +117,22 @@ hipError_t launch_dispatch_bf16(const void* x, int64_t x_stride, int32_t bs, int
   const int64_t xs = x_stride / 8, os = expand_x_stride / 8;
   switch (kmax_for(k)) {
     case 2:
-      dispatch_bf16_kernel<kThreads, kVpt, 2><<<grid, kThreads, 0, stream>>>(
+      launch_kernel(dispatch_bf16_kernel<kThreads, kVpt, 2>, grid, kThreads, stream,
           xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
           capacity_rows, status);
       break;
     case 4:
-      dispatch_bf16_kernel<kThreads, kVpt, 4><<<grid, kThreads, 0, stream>>>(
+      launch_kernel(dispatch_bf16_kernel<kThreads, kVpt, 4>, grid, kThreads, stream,
           xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
           capacity_rows, status);
       break;
     case 8:
-      dispatch_bf16_kernel<kThreads, kVpt, 8><<<grid, kThreads, 0, stream>>>(
+      launch_kernel(dispatch_bf16_kernel<kThreads, kVpt, 8>, grid, kThreads, stream,
           xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
           capacity_rows, status);
       break;
     default:
-      dispatch_bf16_kernel<kThreads, kVpt, 16><<<grid, kThreads, 0, stream>>>(
+      launch_kernel(dispatch_bf16_kernel<kThreads, kVpt, 16>, grid, kThreads, stream,
           xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
           capacity_rows, status);
       break;
@@ -156,22 +156,22 @@ hipError_t launch_dispatch_fp8(const void* x, int64_t x_stride, int32_t bs, int3
   const int32_t nblk = hidden / 128;
   switch (kmax_for(k)) {
     case 2:
-      dispatch_fp8_kernel<kThreads, 2><<<grid, kThreads, 0, stream>>>(
+      launch_kernel(dispatch_fp8_kernel<kThreads, 2>, grid, kThreads, stream,
           xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
           quant_scales, nblk, capacity_rows, status);
       break;
     case 4:
-      dispatch_fp8_kernel<kThreads, 4><<<grid, kThreads, 0, stream>>>(
+      launch_kernel(dispatch_fp8_kernel<kThreads, 4>, grid, kThreads, stream,
           xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
           quant_scales, nblk, capacity_rows, status);
       break;
     case 8:
-      dispatch_fp8_kernel<kThreads, 8><<<grid, kThreads, 0, stream>>>(
+      launch_kernel(dispatch_fp8_kernel<kThreads, 8>, grid, kThreads, stream,
           xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
           quant_scales, nblk, capacity_rows, status);
       break;
     default:
-      dispatch_fp8_kernel<kThreads, 16><<<grid, kThreads, 0, stream>>>(
+      launch_kernel(dispatch_fp8_kernel<kThreads, 16>, grid, kThreads, stream,
           xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
           quant_scales, nblk, capacity_rows, status);
       break;

@@ -240,7 +240,7 @@ hipError_t launch_dispatch_fused_bf16(const void* x, int64_t x_stride, int32_t b
   const int64_t xs = x_stride / 8, os = expand_x_stride / 8;
   const int32_t n = bs * k;
 #define MOE_FUSED_BF16(KM)                                                                    \
-  dispatch_fused_bf16_kernel<kThreads, KM><<<grid, kThreads, 0, stream>>>(                   \
+  launch_kernel(dispatch_fused_bf16_kernel<kThreads, KM>, grid, kThreads, stream,             \
       xv, xs, nvec, nchunks, ids, n, k, num_experts, align, counts, send, expand_idx, status, \
       ov, os, capacity_rows)
   switch (kmax_of(k)) {
@@ -270,7 +270,7 @@ hipError_t launch_dispatch_fused_fp8(const void* x, int64_t x_stride, int32_t bs
   const int32_t nblk = hidden / 128;
   const int32_t n = bs * k;
 #define MOE_FUSED_FP8(KM)                                                                     \
-  dispatch_fused_fp8_kernel<kThreads, KM><<<grid, kThreads, 0, stream>>>(                    \
+  launch_kernel(dispatch_fused_fp8_kernel<kThreads, KM>, grid, kThreads, stream,              \
       xv, xs, ngroups, nchunks, ids, n, k, num_experts, align, counts, send, expand_idx,      \
       status, ov, os, quant_scales, nblk, capacity_rows)
   switch (kmax_of(k)) {

@@ -117,8 +117,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     int32_t* __restrict__ block_flags, int32_t* __restrict__ counts, int32_t* __restrict__ send,
     int32_t* __restrict__ status, ReplicaMap map, RankSplit ranks, ReadAhead ahead,
     int32_t rank_blocks, int32_t ahead_blocks) {
-  if ((int32_t)blockIdx.x >= rank_blocks) {  // read-ahead workgroup: first half
-    read_ahead(ahead, rank_blocks, ahead_blocks, 0, ahead.vecs / 2);
+  if ((int32_t)blockIdx.x >= rank_blocks) {  // read-ahead workgroup: vectors [0, split)
+    read_ahead(ahead, rank_blocks, ahead_blocks, 0, ahead.split);
     return;
   }
   __shared__ unsigned long long mask[kLayoutWaves][kMaxExperts];  // 32 KB
@@ -243,8 +243,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
     const int32_t* __restrict__ block_flags, int32_t* __restrict__ expand_idx,
     int32_t* __restrict__ counts, int32_t* __restrict__ send, int32_t* __restrict__ status,
     RankSplit ranks, ReadAhead ahead, int32_t ahead_blocks) {
-  if ((int32_t)blockIdx.x >= nblocks) {  // read-ahead workgroup: second half
-    read_ahead(ahead, nblocks, ahead_blocks, ahead.vecs / 2, ahead.vecs);
+  if ((int32_t)blockIdx.x >= nblocks) {  // read-ahead workgroup: vectors [split, vecs)
+    read_ahead(ahead, nblocks, ahead_blocks, ahead.split, ahead.vecs);
     return;
   }
   __shared__ int base[kMaxExperts];
@@ -353,7 +353,7 @@ void launch_rank(const LayoutPlan& plan, const int32_t* ids, int32_t k, int32_t 
                  int32_t* expand_idx, int32_t* hist, int32_t* bflags, int32_t* counts,
                  int32_t* send, int32_t* status, const ReplicaMap& map, const RankSplit& ranks,
                  hipStream_t stream, const ReadAhead& ahead, int32_t ahead_blocks) {
-  layout_rank_kernel<R><<<plan.blocks + ahead_blocks, kLayoutThreads, 0, stream>>>(
+  launch_kernel(layout_rank_kernel<R>, plan.blocks + ahead_blocks, kLayoutThreads, stream,
       ids, (int32_t)plan.n_pairs, k, E, align, expand_idx, hist, bflags, counts, send, status,
       map, ranks, ahead, plan.blocks, ahead_blocks);
 }
@@ -395,7 +395,7 @@ hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int
   if (err != hipSuccess || plan.blocks <= 1) return err;
   // The finalize pass looks pairs up by the id they were ranked under.
   const int32_t* ranked_ids = map.offsets != nullptr ? map.out : ids;
-  layout_finalize_kernel<<<plan.blocks + ahead_blocks, kLayoutThreads, 0, stream>>>(
+  launch_kernel(layout_finalize_kernel, plan.blocks + ahead_blocks, kLayoutThreads, stream,
       ranked_ids, (int32_t)plan.n_pairs, num_experts, align, (int32_t)plan.pairs_per_block,
       plan.blocks, hist, bflags, expand_idx, counts, send, status, ranks, ahead, ahead_blocks);
   return hipGetLastError();

@@ -3,6 +3,7 @@
 // in api.hip calls after validating its arguments.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -220,8 +221,13 @@ struct RankSplit {
 // kReadAheadMaxBytes are read ahead (half the cache).
 struct ReadAhead {
   const u32x4* base = nullptr;
-  int64_t vecs = 0;  // 16-byte vectors, from base
+  int64_t vecs = 0;   // 16-byte vectors, from base
+  int64_t split = 0;  // the rank launch reads [0, split), the finalize launch [split, vecs)
 };
+#ifndef MOE_READ_AHEAD_RANK_PERCENT
+#define MOE_READ_AHEAD_RANK_PERCENT 50
+#endif
+constexpr int kReadAheadRankPercent = MOE_READ_AHEAD_RANK_PERCENT;
 constexpr int kReadAheadMaxBlocks = 240;  // of the 256 compute units, with the ranking workgroups
 constexpr int64_t kReadAheadMaxBytes = int64_t(128) << 20;
 constexpr int kReadAheadUnroll = 16;      // loads in flight per thread
@@ -246,6 +252,26 @@ __device__ __forceinline__ void read_ahead(const ReadAhead& ra, int32_t first_bl
     for (int u = 0; u < kReadAheadUnroll; ++u) acc ^= t[u][0] ^ t[u][1] ^ t[u][2] ^ t[u][3];
   }
   __asm__ volatile("" : : "v"(acc));
+}
+
+// ---- launches ----------------------------------------------------------------
+// Every kernel of the library is launched through launch_kernel.  When the
+// calling host thread has event pairs bound by moe_time_next_launches, the
+// launch takes the next pair and goes through hipExtLaunchKernel, which
+// stamps the two events with the kernel's own start and end; otherwise it is
+// a plain launch.
+bool take_launch_events(hipEvent_t* start, hipEvent_t* stop);
+
+template <typename... Params, typename... Args>
+inline void launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t stream,
+                          Args... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "kernel argument count");
+  hipEvent_t start = nullptr, stop = nullptr;
+  if (take_launch_events(&start, &stop))
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0,
+                          static_cast<Params>(args)...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, static_cast<Params>(args)...);
 }
 
 LayoutPlan plan_layout(int32_t bs, int32_t k);

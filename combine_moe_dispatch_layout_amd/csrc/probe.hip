@@ -103,7 +103,7 @@ extern "C" int moe_probe_stream_mix(const void* src, int64_t src_rows_total, voi
   const moe::u32x4* sv = static_cast<const moe::u32x4*>(src);
   moe::u32x4* dv = static_cast<moe::u32x4*>(dst);
 #define MOE_PROBE(RT, WT)                                                                 \
-  moe::stream_mix_kernel<RT, WT><<<grid, moe::kProbeThreads, 0, s>>>(                     \
+  moe::launch_kernel(moe::stream_mix_kernel<RT, WT>, grid, moe::kProbeThreads, s,         \
       sv, src_rows_total, dv, dst_rows_total, nvec, nchunks, reads, writes, src_rows, dst_rows)
   // Compile-time counts for the dispatch (1 : K) and combine (K + 1 : 1) mixes.
   if (reads == 1 && writes == 2) MOE_PROBE(1, 2);

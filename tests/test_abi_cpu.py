@@ -235,6 +235,25 @@ def test_probe_rules(lib):
     assert call(items=0, src=None, dst=None) == 0  # nothing to do
 
 
+def test_time_next_launches_rules(lib):
+    """Binding rules of the kernel-timing hook.  Only host state is touched:
+    the bound handles are never launched with (dropped again with n = 0)."""
+    arr = ctypes.c_void_p * 17
+    starts = arr(*[FAKE + 16 * i for i in range(17)])
+    stops = arr(*[FAKE + 4096 + 16 * i for i in range(17)])
+    assert lib.moe_time_unused_launches() == 0
+    assert lib.moe_time_next_launches(starts, stops, -1) == 1
+    assert lib.moe_time_next_launches(starts, stops, 17) == 1     # at most 16 pairs
+    assert lib.moe_time_next_launches(None, stops, 2) == 1
+    with_null = arr(FAKE, None)
+    assert lib.moe_time_next_launches(starts, with_null, 2) == 1  # NULL among the first n
+    assert lib.moe_time_unused_launches() == 0                    # failures bind nothing
+    assert lib.moe_time_next_launches(starts, stops, 3) == 0
+    assert lib.moe_time_unused_launches() == 3
+    assert lib.moe_time_next_launches(None, None, 0) == 0         # drop
+    assert lib.moe_time_unused_launches() == 0
+
+
 def test_binding_fails_loudly_without_the_library(tmp_path):
     """No CPU fallback: with the library absent, loading it raises (in a
     fresh interpreter whose library path points at an empty folder)."""
