@@ -249,12 +249,14 @@ int moe_dispatch_fused(const void* x, int64_t x_stride, int32_t bs, int32_t hidd
   // The layout launches read the token rows ahead for the scatter (x must be
   // contiguous: the read-ahead walks one range).
   moe::ReadAhead ahead;
+  bool rows_cached = false;  // every token row read ahead
   if (bs > 0 && x_stride == hidden) {
     const int64_t vecs = (int64_t)bs * hidden / 8;
     const int64_t max_vecs = moe::kReadAheadMaxBytes / 16;
     ahead.base = static_cast<const moe::u32x4*>(x);
     ahead.vecs = vecs < max_vecs ? vecs : max_vecs;
     ahead.split = ahead.vecs * moe::kReadAheadRankPercent / 100;
+    rows_cached = ahead.vecs == vecs && moe::read_ahead_runs(plan, ahead);
   }
   hipError_t err = moe::launch_layout(expert_ids, k, num_experts, align, plan, expert_counts,
                                       ep_send_counts, expand_idx, status, workspace,
@@ -263,7 +265,8 @@ int moe_dispatch_fused(const void* x, int64_t x_stride, int32_t bs, int32_t hidd
   if (out_dtype == MOE_BF16)
     return hip_status(moe::launch_dispatch_bf16(x, x_stride, bs, hidden, expert_ids, expand_idx,
                                                 ep_send_counts, k, num_experts, expand_x,
-                                                expand_x_stride, capacity_rows, status, s));
+                                                expand_x_stride, capacity_rows, status, s,
+                                                rows_cached));
   return hip_status(moe::launch_dispatch_fp8(x, x_stride, bs, hidden, expert_ids, expand_idx,
                                              ep_send_counts, k, num_experts, expand_x,
                                              expand_x_stride, capacity_rows, quant_scales,

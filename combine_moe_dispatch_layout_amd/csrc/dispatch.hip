@@ -14,13 +14,16 @@
 namespace moe {
 namespace {
 
-template <int THREADS, int VPT, int KMAX>
+// LDS_INTS sizes the send-count array; a larger array than the counts need
+// only serves to cap how many workgroups share a compute unit.
+template <int THREADS, int VPT, int KMAX, int LDS_INTS>
 __global__ __launch_bounds__(THREADS) void dispatch_bf16_kernel(
     const u32x4* __restrict__ x, int64_t xs, int32_t nvec, int32_t nchunks,
     const int32_t* __restrict__ ids, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ send, int32_t k, int32_t E, u32x4* __restrict__ out, int64_t os,
     int64_t cap, int32_t* status) {
-  __shared__ int send_lds[kMaxExperts + 1];
+  static_assert(LDS_INTS >= kMaxExperts + 1, "send counts must fit");
+  __shared__ int send_lds[LDS_INTS];
   const int32_t t = blockIdx.x / nchunks;
   const int32_t chunk = blockIdx.x - t * nchunks;
   PairMeta meta;
@@ -99,17 +102,23 @@ __global__ __launch_bounds__(THREADS) void dispatch_fp8_kernel(
 
 int kmax_for(int32_t k) { return k <= 2 ? 2 : k <= 4 ? 4 : k <= 8 ? 8 : 16; }
 
-}  // namespace
-
-hipError_t launch_dispatch_bf16(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
-                                const int32_t* ids, const int32_t* expand_idx,
-                                const int32_t* send, int32_t k, int32_t num_experts,
-                                void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
-                                int32_t* status, hipStream_t stream) {
-  constexpr int kThreads = MOE_DISPATCH_THREADS;
+// Launch shape of the bf16 scatter.  With the token rows already in the
+// Infinity Cache (read ahead by the layout launches), the scatter is bound
+// by its row writes alone, and HBM takes them faster from fewer waves in
+// flight, which write a narrower window of destination rows: 64-thread
+// workgroups holding 19 KB of LDS each, so that at most 8 share a compute
+// unit (2 waves per SIMD).  Rows that still come from HBM need the latency
+// hiding of full occupancy, so they keep 128-thread workgroups with only
+// the send counts in LDS.
+template <int THREADS, int LDS_INTS>
+hipError_t launch_bf16_shape(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
+                             const int32_t* ids, const int32_t* expand_idx, const int32_t* send,
+                             int32_t k, int32_t num_experts, void* expand_x,
+                             int64_t expand_x_stride, int64_t capacity_rows, int32_t* status,
+                             hipStream_t stream) {
   constexpr int kVpt = MOE_DISPATCH_VPT;
   const int32_t nvec = hidden / 8;  // 16-byte vectors per row
-  const int32_t nchunks = (nvec + kThreads * kVpt - 1) / (kThreads * kVpt);
+  const int32_t nchunks = (nvec + THREADS * kVpt - 1) / (THREADS * kVpt);
   const int32_t n_items = bs * nchunks;
   const dim3 grid((uint32_t)n_items);
   const u32x4* xv = static_cast<const u32x4*>(x);
@@ -117,27 +126,46 @@ hipError_t launch_dispatch_bf16(const void* x, int64_t x_stride, int32_t bs, int
   const int64_t xs = x_stride / 8, os = expand_x_stride / 8;
   switch (kmax_for(k)) {
     case 2:
-      launch_kernel(dispatch_bf16_kernel<kThreads, kVpt, 2>, grid, kThreads, stream,
+      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 2, LDS_INTS>, grid, THREADS, stream,
           xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
           capacity_rows, status);
       break;
     case 4:
-      launch_kernel(dispatch_bf16_kernel<kThreads, kVpt, 4>, grid, kThreads, stream,
+      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 4, LDS_INTS>, grid, THREADS, stream,
           xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
           capacity_rows, status);
       break;
     case 8:
-      launch_kernel(dispatch_bf16_kernel<kThreads, kVpt, 8>, grid, kThreads, stream,
+      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 8, LDS_INTS>, grid, THREADS, stream,
           xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
           capacity_rows, status);
       break;
     default:
-      launch_kernel(dispatch_bf16_kernel<kThreads, kVpt, 16>, grid, kThreads, stream,
+      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 16, LDS_INTS>, grid, THREADS, stream,
           xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
           capacity_rows, status);
       break;
   }
   return hipGetLastError();
+}
+
+constexpr int kCachedRowsThreads = 64;
+constexpr int kCachedRowsLdsInts = 19456 / 4;  // 8 workgroups in a compute unit's 160 KB
+
+}  // namespace
+
+hipError_t launch_dispatch_bf16(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
+                                const int32_t* ids, const int32_t* expand_idx,
+                                const int32_t* send, int32_t k, int32_t num_experts,
+                                void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
+                                int32_t* status, hipStream_t stream, bool rows_cached) {
+  if (rows_cached)
+    return launch_bf16_shape<kCachedRowsThreads, kCachedRowsLdsInts>(
+        x, x_stride, bs, hidden, ids, expand_idx, send, k, num_experts, expand_x,
+        expand_x_stride, capacity_rows, status, stream);
+  return launch_bf16_shape<MOE_DISPATCH_THREADS, kMaxExperts + 1>(
+      x, x_stride, bs, hidden, ids, expand_idx, send, k, num_experts, expand_x,
+      expand_x_stride, capacity_rows, status, stream);
 }
 
 hipError_t launch_dispatch_fp8(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,

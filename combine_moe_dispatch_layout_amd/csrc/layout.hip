@@ -365,12 +365,8 @@ hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int
                          int32_t* expand_idx, int32_t* status, void* workspace,
                          const ReplicaMap& map, const RankSplit& ranks, hipStream_t stream,
                          const ReadAhead& ahead) {
-  // Read-ahead workgroups only ride along the two-launch layout, and only
-  // while the ranking workgroups leave compute units free.
   const int32_t ahead_blocks =
-      (plan.blocks > 1 && ahead.vecs > 0 && plan.blocks < kReadAheadMaxBlocks)
-          ? kReadAheadMaxBlocks - plan.blocks
-          : 0;
+      read_ahead_runs(plan, ahead) ? kReadAheadMaxBlocks - plan.blocks : 0;
   int32_t* hist = nullptr;
   int32_t* bflags = nullptr;
   if (plan.blocks > 1) {

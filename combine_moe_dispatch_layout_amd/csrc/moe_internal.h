@@ -275,6 +275,12 @@ inline void launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, hipS
 }
 
 LayoutPlan plan_layout(int32_t bs, int32_t k);
+
+// Read-ahead workgroups only ride along the two-launch layout, and only
+// while the ranking workgroups leave compute units free.
+inline bool read_ahead_runs(const LayoutPlan& plan, const ReadAhead& ahead) {
+  return plan.blocks > 1 && ahead.vecs > 0 && plan.blocks < kReadAheadMaxBlocks;
+}
 size_t layout_workspace_bytes(const LayoutPlan& p, int32_t num_experts);
 
 hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int32_t align,
@@ -307,7 +313,7 @@ hipError_t launch_dispatch_bf16(const void* x, int64_t x_stride, int32_t bs, int
                                 const int32_t* ids, const int32_t* expand_idx,
                                 const int32_t* send, int32_t k, int32_t num_experts,
                                 void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
-                                int32_t* status, hipStream_t stream);
+                                int32_t* status, hipStream_t stream, bool rows_cached = false);
 
 hipError_t launch_dispatch_fp8(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
                                const int32_t* ids, const int32_t* expand_idx,

@@ -128,6 +128,54 @@ def test_two_launch_paths_equal_the_separate_calls():
             assert torch.equal(res[1][slots], fused[2][slots])
 
 
+@pytest.mark.parametrize("bs,h,e,k", [
+    (300, 1056, 40, 8),      # 2400 pairs; 132 vectors per row: ragged last 64-thread chunk
+    (700, 512, 64, 8),
+    (1024, 7168, 256, 8),    # the prefill row width
+    (5000, 32, 8, 1),        # rows of 4 vectors: most threads of each workgroup idle
+])
+def test_two_launch_path_matches_the_oracle(bs, h, e, k):
+    """Batches above 2048 pairs with contiguous rows: the layout launches
+    read every row ahead and the scatter runs in its cache-resident launch
+    shape (64-thread workgroups, LDS-capped occupancy)."""
+    rng = np.random.default_rng(bs + h)
+    ids = random_ids(rng, bs, e, k)
+    assert check_against_oracle(ids, random_bf16(rng, (bs, h)), e, 128) == 0
+
+
+def test_two_launch_path_guard_and_hot_experts():
+    rng = np.random.default_rng(9)
+    bs, h, e, k = 700, 256, 16, 8
+    ids = random_ids(rng, bs, e, k)
+    m_pad = int(oracle.layout(ids, e, 128)[1][-1])   # padded rows the layout uses
+    f = check_against_oracle(ids, random_bf16(rng, (bs, h)), e, 128, cap=m_pad - 200,
+                             canary_rows=64)
+    assert f & oracle.FLAG_GUARD
+    hot = np.tile(np.arange(k, dtype=np.int32), (bs, 1))   # every token to experts 0..7
+    assert check_against_oracle(hot, random_bf16(rng, (bs, h)), e, 128) == 0
+
+
+def test_two_launch_path_strided_rows():
+    """Rows with a stride beyond the row width are not read ahead, so the
+    scatter keeps its full-occupancy shape; results as for contiguous rows."""
+    import combine_moe_dispatch_layout_amd as moe
+    rng = np.random.default_rng(10)
+    bs, h, e, k = 600, 512, 64, 8
+    ids = random_ids(rng, bs, e, k)
+    wide = random_bf16(rng, (bs, h + 64))
+    x = to_dev_bf16(wide)[:, :h]
+    cap = oracle.capacity(bs, k, e, 128)
+    c, s, r, f = oracle.layout(ids, e, 128)
+    ref_x, _ = oracle.dispatch_bf16(np.ascontiguousarray(wide[:, :h]), ids, r, s, e, cap)
+    buf = torch.full((cap, h), oracle.SENTINEL_BF16, dtype=torch.int16,
+                     device=DEV).view(torch.bfloat16)
+    lay, _ = moe.moe_dispatch_fused(x, torch.from_numpy(ids).to(DEV), e, 128, expand_x=buf,
+                                    capacity_rows=cap)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(lay.expand_idx.cpu().numpy(), r)
+    np.testing.assert_array_equal(bits_of(buf), ref_x)
+
+
 def test_empty_batch_writes_zero_layout():
     import combine_moe_dispatch_layout_amd as moe
     x = torch.empty((0, 128), dtype=torch.bfloat16, device=DEV)
