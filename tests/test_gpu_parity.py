@@ -409,6 +409,22 @@ def test_workload_full_size(name):
         # every dispatched row equals its token's row, bit for bit
         assert torch.equal(ex[slots].view(torch.int16), x_d[tok].view(torch.int16))
 
+    # moe_dispatch_fused, the call the benchmark times (one launch for decode
+    # sizes; else layout launches that read the rows ahead, then the scatter
+    # in its cache-resident or its full-occupancy shape): the same layout and
+    # the same dispatched rows
+    fused = moe.moe_dispatch_fused(x_d, ids_d, w.experts, w.align, capacity_rows=cap,
+                                   out_dtype="fp8" if w.fp8 else "bf16")
+    torch.cuda.synchronize()
+    for a, b in zip(lay, fused[0]):
+        assert torch.equal(a, b)
+    if w.fp8:
+        assert torch.equal(fused[1][slots], codes[slots])
+        assert torch.equal(fused[2][slots], qs[slots])
+    else:
+        assert torch.equal(fused[1][slots].view(torch.int16), x_d[tok].view(torch.int16))
+    del fused
+
     # combine
     if w.identity_experts:
         y_d = ex
