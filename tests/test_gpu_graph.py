@@ -8,7 +8,7 @@ into the captured buffers, and eager library calls plus a device
 synchronisation run between replays.  Combine consumes the dispatched rows
 (identity experts), so the replay covers the whole chain; both the one-launch
 layout (<= 2048 pairs) and the two-launch layout with its workspace are
-captured.
+captured, through the separate calls and through moe_dispatch_fused.
 """
 
 import numpy as np
@@ -46,12 +46,14 @@ def make_inputs(rng, bs, hidden, e, k, with_shared):
     return ids, scales, x, shared
 
 
+@pytest.mark.parametrize("path", ["separate", "fused"])
 @pytest.mark.parametrize("bs,hidden,e,k,with_shared", [
-    (40, 256, 16, 4, True),       # one-launch layout
-    (700, 384, 64, 8, False),     # two-launch layout, three ranking workgroups
+    (40, 256, 16, 4, True),       # one-launch layout (fused: one launch for both)
+    (700, 384, 64, 8, False),     # two-launch layout, three ranking workgroups (fused: with
+                                  # the rows read ahead and the cache-resident scatter shape)
     (128, 7168, 256, 8, True),    # decode shape
 ])
-def test_captured_step_replays_match_the_oracle(bs, hidden, e, k, with_shared):
+def test_captured_step_replays_match_the_oracle(bs, hidden, e, k, with_shared, path):
     import combine_moe_dispatch_layout_amd as moe
     moe.load_library()
     dev = torch.device("cuda", 0)
@@ -73,9 +75,13 @@ def test_captured_step_replays_match_the_oracle(bs, hidden, e, k, with_shared):
     out = torch.empty((bs, hidden), dtype=torch.bfloat16, device=dev)
 
     def step():
-        moe.moe_dispatch_layout(ids, e, 128, out=lay, workspace=ws)
-        moe.moe_dispatch(x, ids, lay.expand_idx, lay.ep_send_counts, e, expand_x=expand_x,
-                         capacity_rows=cap)
+        if path == "fused":
+            moe.moe_dispatch_fused(x, ids, e, 128, out=lay, capacity_rows=cap,
+                                   expand_x=expand_x, workspace=ws)
+        else:
+            moe.moe_dispatch_layout(ids, e, 128, out=lay, workspace=ws)
+            moe.moe_dispatch(x, ids, lay.expand_idx, lay.ep_send_counts, e, expand_x=expand_x,
+                             capacity_rows=cap)
         moe.moe_combine(expand_x, ids, lay.expand_idx, lay.ep_send_counts, scales, shared, e,
                         out=out)
 
