@@ -1,6 +1,8 @@
 // api.hip -- the C ABI declared in include/moe_dispatch.h: host-side argument
-// checks, workspace sizing and kernel launches.  No call allocates, keeps
-// state or synchronises.
+// checks, workspace sizing and kernel launches.  No call allocates or
+// synchronises, and none keeps state between calls beyond the timing event
+// pairs that moe_time_next_launches (include/moe_probe.h) binds per host
+// thread.
 //
 // Argument rules (each failure returns MOE_ERR_INVALID_ARG and enqueues
 // nothing): the npu_moe_distribute_combine page gives 1 <= num_experts <= 512,

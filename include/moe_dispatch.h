@@ -16,7 +16,9 @@
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers owned by the caller (for example
  *    allocated by PyTorch).  The library allocates nothing, keeps no state
- *    between calls and is safe to call from several host threads.
+ *    between calls (apart from the per-thread timing events of
+ *    moe_time_next_launches in moe_probe.h, a measurement aid) and is safe
+ *    to call from several host threads.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  A
  *    call validates its arguments on the host, enqueues its kernels on
  *    `stream` and returns; it never synchronises.  Buffers must stay alive
@@ -238,7 +240,10 @@ int moe_dispatch(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
  * latency bound, then also read the token rows x ahead (ordinary loads, at
  * most 128 MB, x contiguous) so that the scatter finds them in the 256 MB
  * Infinity Cache instead of interleaving row reads from HBM with its
- * writes.  HBM still reads x once.
+ * writes.  HBM still reads x once.  When every row was read ahead, the bf16
+ * scatter runs with fewer waves in flight (at most 8 workgroups of 64
+ * threads per compute unit), which narrows the window of destination rows
+ * being written at once.
  *
  *  x, x_stride, bs, hidden                   as for moe_dispatch.
  *  expert_ids, k, num_experts, align         as for moe_dispatch_layout.
