@@ -120,6 +120,18 @@ def read_traffic(workload):
 
 # ---------------------------------------------------------------- CPU baseline
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, budget_s, threads=1):
     """The oracle as it stands (plain C loops, gcc -O2), timed on this host
     over whole passes of the workload until the budget is spent.  With
@@ -135,9 +147,9 @@ def cpu_baseline(w, budget_s, threads=1):
     inp = workloads.make(w, rows_y=cap)
     ids, sc = inp["expert_ids"], inp["expert_scales"]
     x = workloads.bits(inp["x"])
-    y = workloads.bits(inp["y"])
     sh = None if inp["shared"] is None else workloads.bits(inp["shared"])
     out = np.full((cap, w.hidden), oracle.SENTINEL_BF16, np.uint16)  # pages touched up front
+    y = out if w.identity_experts else workloads.bits(inp["y"])  # identity experts: y = dispatched rows
     k = w.topk
     cuts = [w.bs * i // threads for i in range(threads + 1)]
     pool = concurrent.futures.ThreadPoolExecutor(threads) if threads > 1 else None
@@ -167,7 +179,8 @@ def cpu_baseline(w, budget_s, threads=1):
     how = "single thread" if threads == 1 else (
         f"{threads} threads over token slices (layout serial)")
     return {"value": round(b / t / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "tokens_per_s": round(w.bs / t, 1), "ms_per_pass": round(t * 1e3, 2),
+            "cpu_model": cpu_model(), "tokens_per_s": round(w.bs / t, 1),
+            "ms_per_pass": round(t * 1e3, 2),
             "sample": f"whole {w.name} batch ({w.bs} tokens: layout + bf16 dispatch + "
                       f"combine), {len(times)} passes in {time.perf_counter() - t_start:.1f} s, "
                       f"median pass, {how}"}
