@@ -231,7 +231,7 @@ hipError_t launch_dispatch_fused_bf16(const void* x, int64_t x_stride, int32_t b
                                       int32_t* send, int32_t* expand_idx, int32_t* status,
                                       void* expand_x, int64_t expand_x_stride,
                                       int64_t capacity_rows, hipStream_t stream) {
-  constexpr int kThreads = MOE_DISPATCH_THREADS;
+  constexpr int kThreads = MOE_FUSED_THREADS;
   const int32_t nvec = hidden / 8;
   const int32_t nchunks = (nvec + kThreads - 1) / kThreads;
   const dim3 grid((uint32_t)(bs * nchunks));

@@ -50,6 +50,9 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 #ifndef MOE_FP8_THREADS
 #define MOE_FP8_THREADS 256
 #endif
+#ifndef MOE_FUSED_THREADS
+#define MOE_FUSED_THREADS 256      // threads per one-launch layout + bf16 scatter workgroup
+#endif
 #ifndef MOE_NT_STORES
 #define MOE_NT_STORES 1            // write-once outputs bypass cache retention
 #endif
