@@ -128,19 +128,22 @@ def test_two_launch_paths_equal_the_separate_calls():
             assert torch.equal(res[1][slots], fused[2][slots])
 
 
-@pytest.mark.parametrize("bs,h,e,k", [
-    (300, 1056, 40, 8),      # 2400 pairs; 132 vectors per row: ragged last 64-thread chunk
-    (700, 512, 64, 8),
-    (1024, 7168, 256, 8),    # the prefill row width
-    (5000, 32, 8, 1),        # rows of 4 vectors: most threads of each workgroup idle
+@pytest.mark.parametrize("bs,h,e,k,align", [
+    (300, 1056, 40, 8, 128),   # 2400 pairs; 132 vectors per row: ragged last 64-thread chunk
+    (700, 512, 64, 8, 128),
+    (1024, 7168, 256, 8, 128), # the prefill row width
+    (5000, 32, 8, 1, 128),     # rows of 4 vectors: most threads of each workgroup idle
+    (300, 256, 512, 16, 128),  # widest top-K, most experts
+    (1001, 96, 40, 3, 64),     # odd K: tokens straddle the ranking workgroups' ranges
+    (900, 128, 33, 5, 1),      # unpadded segments
 ])
-def test_two_launch_path_matches_the_oracle(bs, h, e, k):
+def test_two_launch_path_matches_the_oracle(bs, h, e, k, align):
     """Batches above 2048 pairs with contiguous rows: the layout launches
     read every row ahead and the scatter runs in its cache-resident launch
     shape (64-thread workgroups, LDS-capped occupancy)."""
     rng = np.random.default_rng(bs + h)
     ids = random_ids(rng, bs, e, k)
-    assert check_against_oracle(ids, random_bf16(rng, (bs, h)), e, 128) == 0
+    assert check_against_oracle(ids, random_bf16(rng, (bs, h)), e, align) == 0
 
 
 def test_two_launch_path_guard_and_hot_experts():
