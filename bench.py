@@ -59,15 +59,17 @@ def parse():
                    help="expert-output format read by the combine (fp8 = e4m3 + scales)")
     p.add_argument("--replicas", type=int, default=0,
                    help="split the N most popular experts into 4 replicas each and use the "
-                        "replica-aware layout (probabilistic replica choice + count gathering)")
+                        "replica-aware layout (probabilistic replica choice + count gathering; "
+                        "moe_dispatch_fused_replicated, or with --separate the two calls)")
     p.add_argument("--sets", type=int, default=0,
                    help="buffer sets rotated across steps (0 = enough that no input stays "
                         "cache-resident between uses; see buffer_sets)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU-oracle sample budget (0 disables the cpu_baseline leg)")
     p.add_argument("--separate", action="store_true",
-                   help="layout and dispatch as two calls (moe_dispatch_layout, moe_dispatch) "
-                        "instead of moe_dispatch_fused")
+                   help="layout and dispatch as two calls (moe_dispatch_layout or "
+                        "moe_dispatch_layout_replicated, then moe_dispatch) instead of "
+                        "moe_dispatch_fused or moe_dispatch_fused_replicated")
     p.add_argument("--fused", action="store_true",
                    help="layout + dispatch through moe_dispatch_fused (the default; one launch "
                         "for batches of at most 2048 pairs, else the layout launches read the "
@@ -279,13 +281,12 @@ def main():
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               "(the path is single-device; no collectives are built)", file=sys.stderr)
         sys.exit(2)
-    if args.fused and (args.separate or args.replicas > 0):
-        print("--fused takes logical expert ids; it does not combine with --separate or "
-              "--replicas", file=sys.stderr)
+    if args.fused and args.separate:
+        print("--fused and --separate exclude each other", file=sys.stderr)
         sys.exit(2)
-    # moe_dispatch_fused is the step's layout + dispatch unless asked otherwise
-    # (the replica-aware layout has no fused form).
-    args.fused = not (args.separate or args.replicas > 0)
+    # moe_dispatch_fused (moe_dispatch_fused_replicated with --replicas) is the
+    # step's layout + dispatch unless asked otherwise.
+    args.fused = not args.separate
     import torch
     if args.copy_probe:
         copy_probe()
@@ -373,6 +374,12 @@ def main():
 
     def front(b):
         """Layout and dispatch of one step; returns the layout."""
+        if args.fused and args.replicas > 0:
+            moe.moe_dispatch_fused_replicated(
+                b["x"], ids, w.experts, rep_off, rep_thr, 1234, w.align, out=b["layout"],
+                replica_ids=rep_ids, capacity_rows=cap, expand_x=b["expand_x"],
+                out_dtype="fp8" if w.fp8 else "bf16", quant_scales=b["scales"], workspace=ws)
+            return b["layout"]
         if args.fused:
             moe.moe_dispatch_fused(b["x"], ids, n_phys, w.align, out=b["layout"],
                                    capacity_rows=cap, expand_x=b["expand_x"],
@@ -532,7 +539,9 @@ def main():
                    "align": w.align, "capacity_rows": cap, "buffer_sets": sets,
                    "x_bytes_between_reuse": 2 * w.bs * w.hidden * (sets - 1),
                    "launch": (f"hip graphs of {EVENT_EVERY} steps" if args.graph else "eager"),
-                   "layout_dispatch": "moe_dispatch_fused" if args.fused else "separate",
+                   "layout_dispatch": (("moe_dispatch_fused_replicated" if args.replicas > 0
+                                        else "moe_dispatch_fused") if args.fused
+                                       else "separate"),
                    "combine_input": "e4m3 + fp32 scales" if fp8_combine else "bf16",
                    "replicas": ({"hot_experts": args.replicas, "per_hot": 4,
                                  "physical": n_phys} if args.replicas > 0 else None),

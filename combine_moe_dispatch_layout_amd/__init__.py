@@ -23,6 +23,9 @@ Entry points (same names as the C ABI):
   ``(Layout, rank_offsets [ws+1])``
 * ``moe_dispatch_layout_replicated(expert_ids, num_experts, replica_offsets,
   replica_thresholds, seed)`` -> ``(replica_ids, Layout over replicas)``
+* ``moe_dispatch_fused_replicated(x, expert_ids, num_experts, replica_offsets,
+  replica_thresholds, seed)`` -> ``(replica_ids, Layout, expand_x[,
+  quant_scales])`` (the replica-aware layout and the dispatch in one call)
 * ``moe_plan_compensation(expert_counts, ep_world_size, tile_cost,
   activation_cost)`` -> dict (host-side 128-aligned chunk-migration plan)
 * ``moe_dispatch_capacity`` / ``moe_dispatch_layout_workspace_size``
@@ -47,7 +50,8 @@ __all__ = [
     "MoeError", "Layout", "library_path", "load_library",
     "moe_dispatch_capacity", "moe_dispatch_layout_workspace_size",
     "moe_dispatch_layout", "moe_dispatch_layout_ep", "moe_dispatch_layout_replicated",
-    "moe_dispatch", "moe_dispatch_fused", "moe_combine", "moe_plan_compensation",
+    "moe_dispatch", "moe_dispatch_fused", "moe_dispatch_fused_replicated", "moe_combine",
+    "moe_plan_compensation",
     "moe_combine_fp8", "moe_probe_stream_mix", "moe_time_next_launches",
     "moe_time_unused_launches",
     "MOE_BF16", "MOE_FP8_E4M3", "MOE_FLAG_ID_RANGE", "MOE_FLAG_DUP_ID", "MOE_FLAG_GUARD",
@@ -108,6 +112,9 @@ def load_library() -> ctypes.CDLL:
         "moe_dispatch_layout_replicated": (ctypes.c_int, [P, i32, i32, i32, P, P, i32,
                                                           ctypes.c_uint64, i32, P, P, P, P, P, P,
                                                           sz, P]),
+        "moe_dispatch_fused_replicated": (ctypes.c_int, [P, i64, i32, i32, P, i32, i32, P, P,
+                                                         i32, ctypes.c_uint64, i32, P, P, P, P,
+                                                         P, i64, i64, i32, P, P, P, sz, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -374,6 +381,65 @@ def moe_dispatch_layout_replicated(expert_ids: torch.Tensor, num_experts: int,
         _stream(expert_ids))
     _check(rc)
     return replica_ids, out
+
+
+def moe_dispatch_fused_replicated(x: torch.Tensor, expert_ids: torch.Tensor, num_experts: int,
+                                  replica_offsets: torch.Tensor,
+                                  replica_thresholds: torch.Tensor, seed: int,
+                                  align: int = 128, *, out: Optional[Layout] = None,
+                                  replica_ids: Optional[torch.Tensor] = None,
+                                  capacity_rows: Optional[int] = None, out_dtype: str = "bf16",
+                                  expand_x: Optional[torch.Tensor] = None,
+                                  quant_scales: Optional[torch.Tensor] = None,
+                                  workspace: Optional[torch.Tensor] = None):
+    """moe_dispatch_layout_replicated + moe_dispatch over the replicas in one
+    call.  Returns ``(replica_ids, layout, expand_x)`` or ``(replica_ids,
+    layout, expand_x, quant_scales)``."""
+    _need(x, torch.bfloat16, "x", contiguous=False)
+    _need(expert_ids, torch.int32, "expert_ids")
+    _need(replica_offsets, torch.int32, "replica_offsets")
+    if replica_thresholds.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("replica_thresholds must hold uint32 bit patterns (int32 or uint32)")
+    _need(replica_thresholds, replica_thresholds.dtype, "replica_thresholds")
+    if expert_ids.dim() != 2 or expert_ids.shape[0] != x.shape[0]:
+        raise ValueError("expert_ids must be [BS, K] with BS = x.shape[0]")
+    bs, hidden = x.shape
+    k = expert_ids.shape[1]
+    p = replica_thresholds.numel()
+    dev = x.device
+    dtype = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "e4m3": MOE_FP8_E4M3}[out_dtype]
+    if out is None:
+        out = Layout(torch.empty(p, dtype=torch.int32, device=dev),
+                     torch.empty(p + 1, dtype=torch.int32, device=dev),
+                     torch.empty(bs * k, dtype=torch.int32, device=dev),
+                     torch.empty(1, dtype=torch.int32, device=dev))
+    if replica_ids is None:
+        replica_ids = torch.empty((bs, k), dtype=torch.int32, device=dev)
+    if capacity_rows is None:
+        capacity_rows = (expand_x.shape[0] if expand_x is not None
+                         else moe_dispatch_capacity(bs, k, p, align))
+    if expand_x is None:
+        expand_x = torch.empty((capacity_rows, hidden),
+                               dtype=torch.bfloat16 if dtype == MOE_BF16 else torch.uint8,
+                               device=dev)
+    if dtype == MOE_FP8_E4M3 and quant_scales is None:
+        quant_scales = torch.empty((capacity_rows, hidden // 128), dtype=torch.float32,
+                                   device=dev)
+    ws_bytes = moe_dispatch_layout_workspace_size(bs, k, p)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    rc = load_library().moe_dispatch_fused_replicated(
+        _ptr(x), _row_stride(x, "x"), bs, hidden, _ptr(expert_ids), k, num_experts,
+        _ptr(replica_offsets), _ptr(replica_thresholds), p, seed & 0xFFFFFFFFFFFFFFFF, align,
+        _ptr(replica_ids), _ptr(out.expert_counts), _ptr(out.ep_send_counts),
+        _ptr(out.expand_idx), _ptr(expand_x), _row_stride(expand_x, "expand_x"), capacity_rows,
+        dtype, _ptr(quant_scales) if dtype == MOE_FP8_E4M3 else None, _ptr(out.status),
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(x))
+    _check(rc)
+    if dtype == MOE_BF16:
+        return replica_ids, out, expand_x
+    return replica_ids, out, expand_x, quant_scales
 
 
 def moe_dispatch_layout_ep(expert_ids: torch.Tensor, num_experts: int, ep_world_size: int,

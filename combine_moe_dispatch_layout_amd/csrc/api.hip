@@ -66,6 +66,59 @@ struct TimedLaunches {
 };
 thread_local TimedLaunches tl_timed;
 
+// Row and scale rules of the scatter's inputs and outputs (bs > 0).
+int scatter_args_check(const void* x, int64_t x_stride, int32_t hidden, const void* expand_x,
+                       int64_t expand_x_stride, int64_t capacity_rows, int32_t out_dtype,
+                       const float* quant_scales) {
+  if (!row_ok(x, x_stride, hidden, 2)) return MOE_ERR_INVALID_ARG;
+  if (capacity_rows > 0 &&
+      !row_ok(expand_x, expand_x_stride, hidden, out_dtype == MOE_BF16 ? 2 : 1))
+    return MOE_ERR_INVALID_ARG;
+  if (capacity_rows > 0 && out_dtype == MOE_FP8_E4M3 &&
+      (quant_scales == nullptr || (reinterpret_cast<uintptr_t>(quant_scales) & 3u) != 0))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// The layout launch(es) over `ranked` experts (through the replica map when
+// it has one), then the scatter of x by `route_ids` (the ids the layout
+// ranked: expert_ids, or the replica ids it writes), on one stream.  The
+// layout launches read contiguous token rows ahead (at most
+// kReadAheadMaxBytes); when every row was read, the bf16 scatter takes its
+// cache-resident launch shape.
+int layout_then_scatter(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
+                        const int32_t* expert_ids, const int32_t* route_ids, int32_t k,
+                        int32_t ranked, int32_t align, const moe::LayoutPlan& plan,
+                        int32_t* counts, int32_t* send, int32_t* expand_idx, void* expand_x,
+                        int64_t expand_x_stride, int64_t capacity_rows, int32_t out_dtype,
+                        float* quant_scales, int32_t* status, void* workspace,
+                        size_t workspace_bytes, const moe::ReplicaMap& map, hipStream_t s) {
+  const size_t need = moe::layout_workspace_bytes(plan, ranked);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return MOE_ERR_WORKSPACE;
+  moe::ReadAhead ahead;
+  bool rows_cached = false;  // every token row read ahead
+  if (bs > 0 && x_stride == hidden) {
+    const int64_t vecs = (int64_t)bs * hidden / 8;
+    const int64_t max_vecs = moe::kReadAheadMaxBytes / 16;
+    ahead.base = static_cast<const moe::u32x4*>(x);
+    ahead.vecs = vecs < max_vecs ? vecs : max_vecs;
+    ahead.split = ahead.vecs * moe::kReadAheadRankPercent / 100;
+    rows_cached = ahead.vecs == vecs && moe::read_ahead_runs(plan, ahead);
+  }
+  hipError_t err = moe::launch_layout(expert_ids, k, ranked, align, plan, counts, send,
+                                      expand_idx, status, workspace, map, moe::RankSplit{}, s,
+                                      ahead);
+  if (err != hipSuccess || bs == 0) return hip_status(err);
+  if (out_dtype == MOE_BF16)
+    return hip_status(moe::launch_dispatch_bf16(x, x_stride, bs, hidden, route_ids, expand_idx,
+                                                send, k, ranked, expand_x, expand_x_stride,
+                                                capacity_rows, status, s, rows_cached));
+  return hip_status(moe::launch_dispatch_fp8(x, x_stride, bs, hidden, route_ids, expand_idx,
+                                             send, k, ranked, expand_x, expand_x_stride,
+                                             capacity_rows, quant_scales, status, s));
+}
+
 }  // namespace
 
 namespace moe {
@@ -224,13 +277,9 @@ int moe_dispatch_fused(const void* x, int64_t x_stride, int32_t bs, int32_t hidd
   if (expert_counts == nullptr || ep_send_counts == nullptr) return MOE_ERR_INVALID_ARG;
   if (bs > 0) {
     if (expert_ids == nullptr || expand_idx == nullptr) return MOE_ERR_INVALID_ARG;
-    if (!row_ok(x, x_stride, hidden, 2)) return MOE_ERR_INVALID_ARG;
-    if (capacity_rows > 0 &&
-        !row_ok(expand_x, expand_x_stride, hidden, out_dtype == MOE_BF16 ? 2 : 1))
-      return MOE_ERR_INVALID_ARG;
-    if (capacity_rows > 0 && out_dtype == MOE_FP8_E4M3 &&
-        (quant_scales == nullptr || (reinterpret_cast<uintptr_t>(quant_scales) & 3u) != 0))
-      return MOE_ERR_INVALID_ARG;
+    const int err = scatter_args_check(x, x_stride, hidden, expand_x, expand_x_stride,
+                                       capacity_rows, out_dtype, quant_scales);
+    if (err != MOE_OK) return err;
   }
   const moe::LayoutPlan plan = moe::plan_layout(bs, k);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -245,34 +294,49 @@ int moe_dispatch_fused(const void* x, int64_t x_stride, int32_t bs, int32_t hidd
         quant_scales, s));
   }
   // Otherwise: the layout launch(es), then the scatter, on the same stream.
-  const size_t need = moe::layout_workspace_bytes(plan, num_experts);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
-    return MOE_ERR_WORKSPACE;
-  // The layout launches read the token rows ahead for the scatter (x must be
-  // contiguous: the read-ahead walks one range).
-  moe::ReadAhead ahead;
-  bool rows_cached = false;  // every token row read ahead
-  if (bs > 0 && x_stride == hidden) {
-    const int64_t vecs = (int64_t)bs * hidden / 8;
-    const int64_t max_vecs = moe::kReadAheadMaxBytes / 16;
-    ahead.base = static_cast<const moe::u32x4*>(x);
-    ahead.vecs = vecs < max_vecs ? vecs : max_vecs;
-    ahead.split = ahead.vecs * moe::kReadAheadRankPercent / 100;
-    rows_cached = ahead.vecs == vecs && moe::read_ahead_runs(plan, ahead);
+  return layout_then_scatter(x, x_stride, bs, hidden, expert_ids, expert_ids, k, num_experts,
+                             align, plan, expert_counts, ep_send_counts, expand_idx, expand_x,
+                             expand_x_stride, capacity_rows, out_dtype, quant_scales, status,
+                             workspace, workspace_bytes, moe::ReplicaMap{}, s);
+}
+
+int moe_dispatch_fused_replicated(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
+                                  const int32_t* expert_ids, int32_t k, int32_t num_experts,
+                                  const int32_t* replica_offsets,
+                                  const uint32_t* replica_thresholds, int32_t num_replicas,
+                                  uint64_t seed, int32_t align, int32_t* replica_ids,
+                                  int32_t* replica_counts, int32_t* ep_send_counts,
+                                  int32_t* expand_idx, void* expand_x, int64_t expand_x_stride,
+                                  int64_t capacity_rows, int32_t out_dtype, float* quant_scales,
+                                  int32_t* status, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  if (!layout_args_ok(bs, k, num_experts, align)) return MOE_ERR_INVALID_ARG;
+  if (!layout_args_ok(bs, k, num_replicas, align)) return MOE_ERR_INVALID_ARG;
+  if (hidden <= 0 || hidden % 32 != 0 || hidden > 65536) return MOE_ERR_INVALID_ARG;
+  if (out_dtype == MOE_FP8_E4M3 && hidden % 128 != 0) return MOE_ERR_INVALID_ARG;
+  if (capacity_rows < 0 || !rows_fit(bs, hidden)) return MOE_ERR_INVALID_ARG;
+  if (replica_counts == nullptr || ep_send_counts == nullptr || replica_offsets == nullptr ||
+      replica_thresholds == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (bs > 0) {
+    if (expert_ids == nullptr || expand_idx == nullptr || replica_ids == nullptr)
+      return MOE_ERR_INVALID_ARG;
+    const int err = scatter_args_check(x, x_stride, hidden, expand_x, expand_x_stride,
+                                       capacity_rows, out_dtype, quant_scales);
+    if (err != MOE_OK) return err;
   }
-  hipError_t err = moe::launch_layout(expert_ids, k, num_experts, align, plan, expert_counts,
-                                      ep_send_counts, expand_idx, status, workspace,
-                                      moe::ReplicaMap{}, moe::RankSplit{}, s, ahead);
-  if (err != hipSuccess || bs == 0) return hip_status(err);
-  if (out_dtype == MOE_BF16)
-    return hip_status(moe::launch_dispatch_bf16(x, x_stride, bs, hidden, expert_ids, expand_idx,
-                                                ep_send_counts, k, num_experts, expand_x,
-                                                expand_x_stride, capacity_rows, status, s,
-                                                rows_cached));
-  return hip_status(moe::launch_dispatch_fp8(x, x_stride, bs, hidden, expert_ids, expand_idx,
-                                             ep_send_counts, k, num_experts, expand_x,
-                                             expand_x_stride, capacity_rows, quant_scales,
-                                             status, s));
+  const moe::LayoutPlan plan = moe::plan_layout(bs, k);
+  moe::ReplicaMap map;
+  map.offsets = replica_offsets;
+  map.thresholds = replica_thresholds;
+  map.n_logical = num_experts;
+  map.seed = seed;
+  map.out = replica_ids;
+  return layout_then_scatter(x, x_stride, bs, hidden, expert_ids, replica_ids, k, num_replicas,
+                             align, plan, replica_counts, ep_send_counts, expand_idx, expand_x,
+                             expand_x_stride, capacity_rows, out_dtype, quant_scales, status,
+                             workspace, workspace_bytes, map, static_cast<hipStream_t>(stream));
 }
 
 int moe_combine(const void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,

@@ -319,6 +319,40 @@ int moe_combine_fp8(const void* expand_x, int64_t expand_x_stride, int64_t capac
                     int32_t num_experts, void* x_out, int32_t* status, void* stream);
 
 /*
+ * The replica-aware layout and the dispatch over replicas in one call: the
+ * results of moe_dispatch_layout_replicated followed by moe_dispatch with
+ * expert_ids = replica_ids and num_experts = num_replicas, on the same
+ * stream, bit for bit (replica ids, counts, offsets, ranks, dispatched rows,
+ * padding rows left unwritten, e4m3 codes and scales, status bits).  As in
+ * moe_dispatch_fused, when the layout takes two launches (bs*k > 2048) they
+ * also read the token rows ahead into the Infinity Cache (x contiguous, at
+ * most 128 MB), and a bf16 scatter of rows that were all read ahead runs
+ * with fewer waves in flight.  Batches of at most 2048 pairs take one layout
+ * launch and the scatter launch.
+ *
+ *  x, x_stride, hidden, expand_x, expand_x_stride, capacity_rows, out_dtype,
+ *  quant_scales               as for moe_dispatch (over num_replicas).
+ *  expert_ids, bs, k, num_experts, replica_offsets, replica_thresholds,
+ *  num_replicas, seed, align, replica_ids, replica_counts, ep_send_counts,
+ *  expand_idx, workspace      as for moe_dispatch_layout_replicated.
+ *  status         out int32 [1] or NULL: MOE_FLAG_ID_RANGE | MOE_FLAG_DUP_ID |
+ *                     MOE_FLAG_REPLICA | MOE_FLAG_GUARD of this call,
+ *                     overwritten.
+ * Returns the first error of the two calls' argument rules (nothing is
+ * enqueued), MOE_ERR_WORKSPACE, MOE_ERR_HIP if a launch fails, else 0.
+ */
+int moe_dispatch_fused_replicated(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
+                                  const int32_t* expert_ids, int32_t k, int32_t num_experts,
+                                  const int32_t* replica_offsets,
+                                  const uint32_t* replica_thresholds, int32_t num_replicas,
+                                  uint64_t seed, int32_t align, int32_t* replica_ids,
+                                  int32_t* replica_counts, int32_t* ep_send_counts,
+                                  int32_t* expand_idx, void* expand_x, int64_t expand_x_stride,
+                                  int64_t capacity_rows, int32_t out_dtype, float* quant_scales,
+                                  int32_t* status, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
  * Compensation planner (host code, host pointers; no GPU involved).  The
  * DeepEP compensation PR (Python section) describes a water-filling
  * chunk-migration planner with expert-affinity batching, a makespan guard, a

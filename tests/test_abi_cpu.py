@@ -187,6 +187,23 @@ def test_layout_replicated_rules(lib):
                                               FAKE, FAKE, FAKE, None, None, 0, None) == 1
 
 
+def test_dispatch_fused_replicated_rules(lib):
+    def call(k=2, e=8, reps=8, hidden=128, dtype=0, offsets=FAKE, thresholds=FAKE,
+             cap=64, expand_x=FAKE, scales=None, bs=4):
+        return lib.moe_dispatch_fused_replicated(
+            FAKE, hidden, bs, hidden, FAKE, k, e, offsets, thresholds, reps, 0, 128, FAKE, FAKE,
+            FAKE, FAKE, expand_x, hidden, cap, dtype, scales, None, None, 0, None)
+
+    assert call(reps=1) == 1                  # k = 2 distinct choices need two replicas
+    assert call(reps=513) == 1
+    assert call(offsets=None) == 1 and call(thresholds=None) == 1
+    assert call(hidden=96, dtype=1) == 1      # e4m3 rows need H % 128 == 0
+    assert call(dtype=1, scales=None) == 1    # e4m3 needs the scales
+    assert call(dtype=7) == 3                 # unsupported output type
+    assert call(hidden=48) == 1               # H % 32
+    assert call(expand_x=FAKE + 8) == 1       # misaligned output rows
+
+
 def test_plain_c_program_uses_the_abi(tmp_path):
     """The header compiles as C99 and a C program links the library and gets
     the documented results from every host-side call (no GPU needed)."""

@@ -596,6 +596,55 @@ def test_replicated_pipeline_round_trip():
     assert torch.equal(out.view(torch.int16), x.view(torch.int16))
 
 
+@pytest.mark.parametrize("bs,h,e,k,max_rep,dtype", [
+    (100, 256, 16, 4, 3, "bf16"),      # one layout launch (<= 2048 pairs)
+    (700, 512, 64, 8, 4, "bf16"),      # two launches, rows read ahead, cache-resident scatter
+    (1200, 1056, 40, 6, 2, "bf16"),    # odd K, ragged row chunks
+    (600, 512, 32, 8, 3, "fp8"),
+    (2048, 7168, 128, 8, 2, "bf16"),   # prefill row width
+])
+def test_fused_replicated_matches_oracle(bs, h, e, k, max_rep, dtype):
+    """moe_dispatch_fused_replicated equals the oracle's replica-aware layout
+    and the oracle's dispatch over replica ids (bf16 rows bit for bit; e4m3
+    codes and scales bit for bit), padding rows untouched."""
+    moe = moe_mod()
+    rng = np.random.default_rng(bs * 3 + k)
+    off, thr = random_replica_table(rng, e, max_rep)
+    p = int(off[-1])
+    assert p <= 512
+    ids = random_ids(rng, bs, e, k)
+    x_bits = oracle.f32_to_bf16_bits(rng.standard_normal((bs, h)).astype(np.float32))
+    seed = 1000 + bs
+    rep, c, s, r, f = oracle.layout_replicated(ids, e, off, thr, seed, 128)
+    cap = oracle.capacity(bs, k, p, 128)
+    if dtype == "bf16":
+        buf = torch.full((cap, h), oracle.SENTINEL_BF16, dtype=torch.int16,
+                         device=DEV).view(torch.bfloat16)
+        grep, lay, ex = moe.moe_dispatch_fused_replicated(
+            bf16_dev(x_bits), dev(ids), e, dev(off), dev(thr.view(np.int32)), seed, 128,
+            expand_x=buf, capacity_rows=cap)
+    else:
+        grep, lay, ex, qs = moe.moe_dispatch_fused_replicated(
+            bf16_dev(x_bits), dev(ids), e, dev(off), dev(thr.view(np.int32)), seed, 128,
+            capacity_rows=cap, out_dtype="fp8")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(grep.cpu().numpy(), rep)
+    np.testing.assert_array_equal(lay.expert_counts.cpu().numpy(), c)
+    np.testing.assert_array_equal(lay.ep_send_counts.cpu().numpy(), s)
+    np.testing.assert_array_equal(lay.expand_idx.cpu().numpy(), r)
+    if dtype == "bf16":
+        ref_x, f2 = oracle.dispatch_bf16(x_bits, rep, r, s, p, cap)
+        assert int(lay.status.cpu()[0]) == (f | f2)
+        np.testing.assert_array_equal(host_bits(ex), ref_x)
+    else:
+        codes_ref, qs_ref, f2 = oracle.dispatch_fp8(x_bits, rep, r, s, p, cap)
+        assert int(lay.status.cpu()[0]) == (f | f2)
+        slots = (s[rep.ravel()] + r)[rep.ravel() >= 0]
+        np.testing.assert_array_equal(ex.cpu().numpy()[slots], codes_ref[slots])
+        np.testing.assert_array_equal(qs.cpu().numpy()[slots].view(np.uint32),
+                                      qs_ref[slots].view(np.uint32))
+
+
 # ------------------------------------------------------------------ rank-partitioned layout
 
 @pytest.mark.parametrize("bs,e,k,ws", [(1, 1, 1, 1), (300, 64, 8, 8), (4096, 256, 8, 8),
