@@ -54,7 +54,9 @@ def build(verbose: bool = False) -> str:
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as pool:
         objs = list(pool.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    exports = os.path.join(CSRC, "exports.map")  # only the moe_* C ABI is exported
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC",
+           f"-Wl,--version-script={exports}", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

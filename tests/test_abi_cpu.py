@@ -50,6 +50,23 @@ def test_library_exports_every_declared_symbol(lib):
         assert getattr(lib, name) is not None
 
 
+def test_library_exports_only_the_c_abi():
+    """The shared library's dynamic symbol table holds the moe_* entry points
+    and nothing else (the kernels and C++ launchers stay local)."""
+    import shutil
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    import combine_moe_dispatch_layout_amd as m
+    out = subprocess.run([nm, "-D", "--defined-only", m.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    names = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert names, "no exported symbols"
+    assert all(n.startswith("moe_") for n in names), sorted(n for n in names
+                                                            if not n.startswith("moe_"))
+    assert names == declared_functions()
+
+
 def test_abi_version_and_status_strings(lib):
     assert lib.moe_abi_version() == 1
     for code in range(5):
