@@ -2,8 +2,9 @@
 device memory from the HIP runtime's C API and every call through the C
 ABI, no Python binding or torch involved.  With identity experts and exact
 binary-fraction weights summing to 1 the combine must return x bit for bit
-(separate calls with one- and two-launch layouts, and the fused entry
-point)."""
+(separate calls with one- and two-launch layouts, the fused entry point,
+the replica-aware fused entry point, and kernel times through
+moe_time_next_launches)."""
 
 import os
 import subprocess
