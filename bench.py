@@ -61,6 +61,9 @@ def parse():
                    help="split the N most popular experts into 4 replicas each and use the "
                         "replica-aware layout (probabilistic replica choice + count gathering; "
                         "moe_dispatch_fused_replicated, or with --separate the two calls)")
+    p.add_argument("--ep", type=int, default=0,
+                   help="rank-partitioned layout: experts split over N destination ranks, "
+                        "moe_dispatch_layout_ep then moe_dispatch (separate calls)")
     p.add_argument("--sets", type=int, default=0,
                    help="buffer sets rotated across steps (0 = enough that no input stays "
                         "cache-resident between uses; see buffer_sets)")
@@ -284,6 +287,12 @@ def main():
     if args.fused and args.separate:
         print("--fused and --separate exclude each other", file=sys.stderr)
         sys.exit(2)
+    if args.ep and (args.replicas > 0 or args.fused):
+        print("--ep runs the separate calls and takes no --replicas or --fused",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.ep:
+        args.separate = True
     # moe_dispatch_fused (moe_dispatch_fused_replicated with --replicas) is the
     # step's layout + dispatch unless asked otherwise.
     args.fused = not args.separate
@@ -352,7 +361,13 @@ def main():
 
     route_ids = rep_ids if args.replicas > 0 else ids
 
+    rank_offsets = (torch.empty(args.ep + 1, dtype=torch.int32, device=dev) if args.ep
+                    else None)
+
     def layout(b):
+        if args.ep:
+            return moe.moe_dispatch_layout_ep(ids, w.experts, args.ep, w.align, out=b["layout"],
+                                              rank_offsets=rank_offsets, workspace=ws)[0]
         if args.replicas > 0:
             return moe.moe_dispatch_layout_replicated(
                 ids, w.experts, rep_off, rep_thr, 1234, w.align, out=b["layout"],
@@ -545,6 +560,7 @@ def main():
                    "combine_input": "e4m3 + fp32 scales" if fp8_combine else "bf16",
                    "replicas": ({"hot_experts": args.replicas, "per_hot": 4,
                                  "physical": n_phys} if args.replicas > 0 else None),
+                   "ep_world_size": args.ep or None,
                    "bytes_per_step": step_bytes},
         "kernel_times": ("combine: timed region; layout and dispatch: 10 eager steps after "
                          "it, events bound to each kernel launch"),
