@@ -80,3 +80,42 @@ def test_failed_call_leaves_pairs_bound():
     assert moe.moe_time_unused_launches() == 2
     moe.moe_time_next_launches([])
     assert moe.moe_time_unused_launches() == 0
+
+
+def test_bindings_are_per_host_thread():
+    """Pairs bound on one host thread are taken only by that thread's
+    launches: a second thread launching meanwhile leaves them bound."""
+    import threading
+
+    import combine_moe_dispatch_layout_amd as moe
+    rng = np.random.default_rng(21)
+    ids = torch.from_numpy(random_ids(rng, 300, 64, 8)).cuda()
+    pairs = new_pairs(4)
+    torch.cuda.synchronize()
+    moe.moe_time_next_launches(pairs)
+    seen = {}
+
+    def other():
+        try:
+            seen["before"] = moe.moe_time_unused_launches()   # nothing bound on this thread
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                moe.moe_dispatch_layout(ids, 64)
+            stream.synchronize()
+            seen["after"] = moe.moe_time_unused_launches()
+        except Exception as err:  # reported below
+            seen["error"] = err
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join(timeout=60)
+    assert "error" not in seen, seen.get("error")
+    assert seen == {"before": 0, "after": 0}
+    assert moe.moe_time_unused_launches() == 4       # this thread's pairs untouched
+    moe.moe_dispatch_layout(ids, 64)                 # 2400 pairs: two layout launches
+    assert moe.moe_time_unused_launches() == 2
+    moe.moe_time_next_launches([])
+    torch.cuda.synchronize()
+    for a, z in pairs[:2]:
+        assert a.elapsed_time(z) > 0
+
