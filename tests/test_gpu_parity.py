@@ -699,6 +699,28 @@ def test_maximum_dimensions():
     np.testing.assert_array_equal(host_bits(ex), oracle.dispatch_bf16(x, ids, r, s, e, cap)[0])
 
 
+def test_maximum_row_two_launch_fused():
+    """moe_dispatch_fused above 2048 pairs at the largest row (H = 65536,
+    E = 512, K = 16): the layout launches read the 26 MB of rows ahead and the
+    scatter runs in its cache-resident shape (128 chunks of 64 threads per
+    row); every element against the oracle."""
+    moe = moe_mod()
+    rng = np.random.default_rng(200)
+    bs, h, e, k, align = 200, 65536, 512, 16, 1
+    ids = random_ids(rng, bs, e, k)
+    x = random_bf16(rng, (bs, h))
+    c, s, r, f = oracle.layout(ids, e, align)
+    cap = oracle.capacity(bs, k, e, align)
+    lay, ex = moe.moe_dispatch_fused(bf16_dev(x), dev(ids), e, align, capacity_rows=cap)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(lay.expert_counts.cpu().numpy(), c)
+    np.testing.assert_array_equal(lay.ep_send_counts.cpu().numpy(), s)
+    np.testing.assert_array_equal(lay.expand_idx.cpu().numpy(), r)
+    assert int(lay.status.cpu()[0]) == f == 0
+    assert cap == bs * k                    # align 1: every row is a real row
+    np.testing.assert_array_equal(host_bits(ex), oracle.dispatch_bf16(x, ids, r, s, e, cap)[0])
+
+
 def test_layout_many_workgroups_every_expert_count():
     """Hundreds of ranking workgroups with E from 1 to 512, so the finalize
     pass's column sums run with 16, 8, 4, 2 and 1 threads per column."""
