@@ -1,12 +1,14 @@
-/* Host-only check of the C ABI from plain C (C99): the header compiles as C,
- * the library links, and the calls that never reach the GPU behave as the
- * header states (size queries, status strings, argument errors, the host
- * planner).  Prints "ok" and exits 0 on success. */
+/* Host-only check of the C ABI from plain C (C99): both headers compile as
+ * C, the library links, and the calls that never reach the GPU behave as the
+ * headers state (size queries, status strings, argument errors, the host
+ * planner, binding and dropping timing events without launching).  Prints
+ * "ok" and exits 0 on success. */
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
 #include "moe_dispatch.h"
+#include "moe_probe.h"
 
 static int failures = 0;
 
@@ -48,6 +50,29 @@ int main(void) {
                      NULL) == MOE_ERR_INVALID_ARG, "combine hidden % 32");
   expect(moe_combine(NULL, 64, 64, NULL, NULL, NULL, NULL, NULL, 0, 0, 64, 2, 8, NULL, NULL,
                      NULL) == MOE_OK, "combine of an empty batch");
+  expect(moe_dispatch_fused(NULL, 64, 4, 64, &fake_ids, 2, 8, 128, counts, send, idx, NULL, 64,
+                            64, 7, NULL, NULL, NULL, 0, NULL) == MOE_ERR_UNSUPPORTED,
+         "fused dispatch dtype");
+  expect(moe_dispatch_fused_replicated(NULL, 64, 4, 64, &fake_ids, 2, 8, NULL, NULL, 8, 0, 128,
+                                       idx, counts, send, idx, NULL, 64, 64, MOE_BF16, NULL,
+                                       NULL, NULL, 0, NULL) == MOE_ERR_INVALID_ARG,
+         "replica-aware fused dispatch without its tables");
+
+  /* measurement support: bindings are checked, and n = 0 drops them */
+  {
+    void* starts[2] = {(void*)&fake_ids, NULL};
+    void* stops[2] = {(void*)&fake_ids, (void*)&fake_ids};
+    expect(moe_time_next_launches(starts, stops, 17) == MOE_ERR_INVALID_ARG, "timing: n > 16");
+    expect(moe_time_next_launches(starts, stops, 2) == MOE_ERR_INVALID_ARG,
+           "timing: NULL event");
+    expect(moe_time_unused_launches() == 0, "timing: nothing bound after errors");
+    expect(moe_time_next_launches(starts, stops, 1) == MOE_OK, "timing: bind one pair");
+    expect(moe_time_unused_launches() == 1, "timing: one pair bound");
+    expect(moe_time_next_launches(NULL, NULL, 0) == MOE_OK, "timing: drop");
+    expect(moe_time_unused_launches() == 0, "timing: dropped");
+  }
+  expect(moe_probe_stream_mix(NULL, 0, NULL, 0, 4, 24, 1, 8, NULL, NULL, NULL) ==
+             MOE_ERR_INVALID_ARG, "probe row bytes not a multiple of 16");
 
   /* planner: one hot expert of 1024 rows between two ranks splits evenly */
   expect(moe_plan_compensation(expert_counts, 4, 2, 8, 10, 0, 16, moves, &n_moves, loads, &before,
