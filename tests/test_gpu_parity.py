@@ -139,6 +139,32 @@ def test_layout_is_deterministic():
         assert torch.equal(cur, ref)
 
 
+def test_whole_step_is_deterministic():
+    """The benchmark's step (moe_dispatch_fused with the read-ahead and the
+    cache-resident scatter, then moe_combine) on the skewed workload, 20
+    times: layout, dispatched rows and output bit for bit the same."""
+    moe = moe_mod()
+    w = workloads.WORKLOADS["skewed"]
+    cap = oracle.capacity(w.bs, w.topk, w.experts, w.align)
+    inp = workloads.make(w, rows_y=cap)
+    ids = dev(inp["expert_ids"])
+    sc = dev(inp["expert_scales"])
+    x, y, sh = inp["x"].to(DEV), inp["y"].to(DEV), inp["shared"].to(DEV)
+    ex = torch.empty((cap, w.hidden), dtype=torch.bfloat16, device=DEV)
+    ref = None
+    for _ in range(20):
+        ex.zero_()
+        lay, _ = moe.moe_dispatch_fused(x, ids, w.experts, w.align, expand_x=ex,
+                                        capacity_rows=cap)
+        out = moe.moe_combine(y, ids, lay.expand_idx, lay.ep_send_counts, sc, sh, w.experts)
+        torch.cuda.synchronize()
+        cur = (torch.cat([lay.expert_counts, lay.ep_send_counts, lay.expand_idx]),
+               ex.view(torch.int16).clone(), out.view(torch.int16))
+        if ref is None:
+            ref = cur
+        assert all(torch.equal(a, b) for a, b in zip(cur, ref))
+
+
 # ------------------------------------------------------------------ dispatch
 
 def run_dispatch_bf16(ids, x_bits, e, align, x_stride=None, out_stride=None, cap=None):
