@@ -230,33 +230,42 @@ def buffer_sets(w, cap, step_bytes, fp8_combine):
     return max(1, min(max(by_cache, by_volume), SET_MEMORY_CAP // per_set, 64))
 
 
-def practical_ceiling(moe, w, launches=16):
+def practical_ceiling(moe, w, slots, cap, launches=16):
     """GB/s of the plain streaming probe with the dispatch's 1 : K and the
     combine's (K + 1) : 1 row mixes at this workload's bf16 row size and
-    token count: all rows in order, and with the K expert-side rows randomly
-    permuted as the real layout scatters them (seeded; the token-side rows
-    stay in order).  Mean kernel time of `launches` launches (at most 16),
-    each timed by HIP events bound to it, after 3 warm-up launches."""
+    token count, with the expert-side rows
+      - in order (`in_order`),
+      - randomly permuted (`random_rows`; seeded), and
+      - at the real layout's slots of this routing (`layout_rows`: tokens in
+        order, each token's K rows where the layout puts them),
+    the token-side rows (x, shared, output) in order.  `slots` is the int64
+    [BS, K] device tensor of the layout's rows.  Mean kernel time of
+    `launches` launches (at most 16), each timed by HIP events bound to it,
+    after 3 warm-up launches."""
     import numpy as np
     import torch
     bs, k, row_bytes = w.bs, w.topk, 2 * w.hidden
     cols = row_bytes // 4
     g = np.random.default_rng(12345)
+    rows_y = max(bs * k, cap)
+    layout_rows = slots.to(torch.int32).contiguous()
     out = {}
     for name, reads, writes in (("dispatch_mix", 1, k), ("combine_mix", k + 1, 1)):
-        src = torch.zeros((bs * reads, cols), dtype=torch.int32, device="cuda")
-        dst = torch.empty((bs * writes, cols), dtype=torch.int32, device="cuda")
-        perm = g.permutation(bs * k).astype(np.int32)
-        if writes > 1:   # dispatch: token rows in order, K copies to random rows
-            rows = {"dst": torch.from_numpy(perm).cuda()}
-        else:            # combine: K random expert rows, then the token's own shared row
-            idx = np.concatenate([perm.reshape(bs, k),
-                                  (bs * k + np.arange(bs, dtype=np.int32))[:, None]], axis=1)
-            rows = {"src": torch.from_numpy(np.ascontiguousarray(idx).ravel()).cuda()}
+        src = torch.zeros((bs if writes > 1 else rows_y + bs, cols), dtype=torch.int32,
+                          device="cuda")
+        dst = torch.empty((rows_y if writes > 1 else bs, cols), dtype=torch.int32, device="cuda")
+        perm = torch.from_numpy(g.permutation(bs * k).astype(np.int32)).cuda().view(bs, k)
+        shared_rows = (rows_y + torch.arange(bs, dtype=torch.int32, device="cuda"))[:, None]
         res = {}
-        for order in ("in_order", "random_rows"):
-            src_rows = rows.get("src") if order == "random_rows" else None
-            dst_rows = rows.get("dst") if order == "random_rows" else None
+        for order, expert_rows in (("in_order", None), ("random_rows", perm),
+                                   ("layout_rows", layout_rows)):
+            if expert_rows is None:   # contiguous: item i's rows i*R .. i*R+R-1
+                src_rows = dst_rows = None
+            elif writes > 1:          # dispatch: token row t, K copies to the expert rows
+                src_rows, dst_rows = None, expert_rows.reshape(-1).contiguous()
+            else:                     # combine: K expert rows, then the token's shared row
+                src_rows = torch.cat([expert_rows, shared_rows], dim=1).reshape(-1).contiguous()
+                dst_rows = None
             run = lambda: moe.moe_probe_stream_mix(src, dst, bs, reads, writes, src_rows,
                                                    dst_rows)
             for _ in range(3):
@@ -583,15 +592,23 @@ def main():
     # The probe models bf16 rows at bandwidth-bound sizes (a decode-sized
     # step is launch-latency bound, and a probe of it says nothing).
     if not (args.no_ceiling or w.fp8 or fp8_combine or step_bytes < MALL_BYTES):
-        ceil = practical_ceiling(moe, w)
+        lay0 = bufs[0]["layout"]
+        slots = (lay0.ep_send_counts[route_ids.reshape(-1).long()].long()
+                 + lay0.expand_idx.long()).view(w.bs, w.topk)
+        ceil = practical_ceiling(moe, w, slots, cap)
         result["practical_ceiling"] = {
             "probe": "moe_probe_stream_mix: plain 16-B streaming kernel, same read:write row mix",
             "unit": "GB/s", **ceil,
             "combine_frac_of_random_rows": round(
                 achieved / ceil["combine_mix"]["random_rows"], 4),
+            "combine_frac_of_layout_rows": round(
+                achieved / ceil["combine_mix"]["layout_rows"], 4),
             "dispatch_frac_of_random_rows": round(
                 nbytes["dispatch"] / (mean(kern_ms["dispatch"]) / 1e3) / 1e9
-                / ceil["dispatch_mix"]["random_rows"], 4) if not args.fused else None}
+                / ceil["dispatch_mix"]["random_rows"], 4) if not args.fused else None,
+            "dispatch_frac_of_layout_rows": round(
+                nbytes["dispatch"] / (mean(kern_ms["dispatch"]) / 1e3) / 1e9
+                / ceil["dispatch_mix"]["layout_rows"], 4) if not args.fused else None}
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
         cores = min(16, len(os.sched_getaffinity(0)))
