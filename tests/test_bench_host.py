@@ -95,6 +95,15 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr
 
 
+@pytest.mark.parametrize("flags", [["--fused", "--separate"], ["--ep", "8", "--replicas", "4"],
+                                   ["--ep", "8", "--fused"]])
+def test_conflicting_options_are_refused(flags):
+    """Refused before anything touches a GPU."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *flags],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2, r.stderr
+
+
 @pytest.mark.parametrize("threads", [1, 2])
 def test_cpu_baseline_leg(bench, threads):
     w = workloads.WORKLOADS["tiny"]
