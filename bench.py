@@ -12,18 +12,17 @@ already resident in HBM when the timed region starts.  Prints ONE JSON line.
 
 `value` is algorithmic bytes per step (real rows only, never padding) divided
 by the measured step time, in GB/s; `tokens_per_s` is tokens per step over the
-same time.  The `roofline` object covers the kernel that moves the most bytes
-(combine): its algorithmic bytes per launch over its mean kernel time, from
-HIP events bound to the combine launch of every 10th step inside the timed
-region (moe_time_next_launches: the runtime stamps them with the kernel's own
-start and end on the launch stream).  `kernels_ms` adds the layout and
-dispatch kernels, timed the same way in 10 steps after the timed region.
+same time.  The timed region holds the steps alone: no event is bound to a
+launch inside it.  The `roofline` object covers the kernel that moves the most
+bytes (combine): its algorithmic bytes per launch over its mean kernel time,
+from HIP events bound to the combine launch (moe_time_next_launches: the
+runtime stamps them with the kernel's own start and end on the launch stream)
+in ROOFLINE_STEPS steps after the timed region.  `kernels_ms` adds the layout
+and dispatch kernels, each launch timed the same way in 10 further steps.
 
 `--separate` runs layout and dispatch as two calls (moe_dispatch_layout,
 moe_dispatch); `--graph` replays the steps as captured HIP graphs of 10 steps
-each, split before the last combine, which events recorded around its
-replay time instead.  `cpu_baseline` times the CPU oracle on the same
-workload.
+each.  `cpu_baseline` times the CPU oracle on the same workload.
 """
 
 from __future__ import annotations
@@ -41,7 +40,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
-EVENT_EVERY = 10        # one combine timed by events every 10 steps
+GRAPH_STEPS = 10        # steps per captured graph (--graph)
+ROOFLINE_STEPS = 20     # steps after the timed region whose combine launch is timed
+BREAKDOWN_STEPS = 10    # steps after those with every kernel launch timed
 METRIC = "dispatch+combine achieved HBM GB/s and tokens/s, H=7168 E=256 K=8 bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_bf16_skewed_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_moe_dispatch_layout_amd", "csrc", f)
@@ -344,9 +345,11 @@ def main():
     yc0 = yc.to(dev) if fp8_combine else None
     ys0 = ys.to(dev) if fp8_combine else None
     sh0 = None if inp["shared"] is None else inp["shared"].to(dev)
+    # Every output of every set is written once here (zero-filled), before
+    # the warm-up, so that no step writes a buffer for the first time.
     bufs = []
     for i in range(sets):
-        ex = torch.empty((cap, w.hidden), dtype=torch.uint8 if w.fp8 else torch.bfloat16,
+        ex = torch.zeros((cap, w.hidden), dtype=torch.uint8 if w.fp8 else torch.bfloat16,
                          device=dev)
         bufs.append({
             "index": i,
@@ -354,18 +357,18 @@ def main():
             "y": ex if y0 is None else (y0 if i == 0 else y0.clone()),
             "y_codes": None if yc0 is None else (yc0 if i == 0 else yc0.clone()),
             "y_scales": None if ys0 is None else (ys0 if i == 0 else ys0.clone()),
-            "scales": (torch.empty((cap, w.hidden // 128), dtype=torch.float32, device=dev)
+            "scales": (torch.zeros((cap, w.hidden // 128), dtype=torch.float32, device=dev)
                        if w.fp8 else None),
             "shared": None if sh0 is None else (sh0 if i == 0 else sh0.clone()),
             "expand_x": ex,
-            "out": torch.empty((w.bs, w.hidden), dtype=torch.bfloat16, device=dev),
-            "layout": moe.Layout(torch.empty(n_phys, dtype=torch.int32, device=dev),
-                                 torch.empty(n_phys + 1, dtype=torch.int32, device=dev),
-                                 torch.empty(w.bs * w.topk, dtype=torch.int32, device=dev),
-                                 torch.empty(1, dtype=torch.int32, device=dev)),
+            "out": torch.zeros((w.bs, w.hidden), dtype=torch.bfloat16, device=dev),
+            "layout": moe.Layout(torch.zeros(n_phys, dtype=torch.int32, device=dev),
+                                 torch.zeros(n_phys + 1, dtype=torch.int32, device=dev),
+                                 torch.zeros(w.bs * w.topk, dtype=torch.int32, device=dev),
+                                 torch.zeros(1, dtype=torch.int32, device=dev)),
         })
     ws_bytes = moe.moe_dispatch_layout_workspace_size(w.bs, w.topk, n_phys)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     route_ids = rep_ids if args.replicas > 0 else ids
@@ -461,66 +464,61 @@ def main():
 
     graphs = None
     if args.graph:
-        # Steps are captured EVENT_EVERY at a time, the way a serving loop
-        # replays a whole pass: graph A holds EVENT_EVERY - 1 whole steps and
-        # the layout + dispatch of the last one, graph B that last step's
-        # combine, so its launch can be bracketed by events on the stream.
-        # One pattern per distinct sequence of buffer sets.  No call
-        # allocates or enqueues a memset when its outputs are given.
-        if args.steps % EVENT_EVERY:
-            print(f"--graph needs --steps to be a multiple of {EVENT_EVERY}", file=sys.stderr)
+        # Steps are captured GRAPH_STEPS at a time, the way a serving loop
+        # replays a whole pass; one graph per distinct sequence of buffer
+        # sets.  No call allocates or enqueues a memset when its outputs are
+        # given.
+        if args.steps % GRAPH_STEPS:
+            print(f"--graph needs --steps to be a multiple of {GRAPH_STEPS}", file=sys.stderr)
             sys.exit(2)
         graphs = []
-        for c in range(sets // math.gcd(sets, EVENT_EVERY)):
-            first = c * EVENT_EVERY
-            head, back = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-            with torch.cuda.graph(head):
-                for j in range(EVENT_EVERY - 1):
-                    b = bufs[(first + j) % sets]
-                    combine(b, front(b))
-                b = bufs[(first + EVENT_EVERY - 1) % sets]
-                lay = front(b)
-            with torch.cuda.graph(back):
-                combine(b, lay)
-            graphs.append((head, back))
-        for head, back in graphs:
-            head.replay()
-            back.replay()
+        for c in range(sets // math.gcd(sets, GRAPH_STEPS)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for j in range(GRAPH_STEPS):
+                    step(bufs[(c * GRAPH_STEPS + j) % sets])
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
         torch.cuda.synchronize()
 
-    # Timed region: K steps on the host clock.  Eager: the combine launch of
-    # every EVENT_EVERY-th step takes HIP events bound to it, which the
-    # runtime stamps with the kernel's own start and end on the launch
-    # stream.  A bound launch adds ~5 us to its step, so not every
-    # step is timed, and the layout and dispatch launches are timed after the
-    # timed region.  Graph replays cannot carry bound events, so there events
-    # recorded on the stream bracket the replay of the graph that holds one
-    # combine launch; they also hold that replay's launch gap.
-    pairs = {i: new_pairs(1)[0] for i in range(0, args.steps, EVENT_EVERY)}
+    # Timed region: exactly K steps on the host clock, synchronised on both
+    # sides, with nothing bound to a launch.  Two events recorded on the
+    # stream at its ends give the same interval on the GPU's clock (without
+    # the host's wake-up after the last kernel).
+    region = new_pairs(1)[0]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    region[0].record(stream)
     if graphs is None:
         for i in range(args.steps):
-            step(bufs[i % sets], pairs.get(i))
+            step(bufs[i % sets])
     else:
-        for c in range(args.steps // EVENT_EVERY):
-            head, back = graphs[c % len(graphs)]
-            ev0, ev1 = pairs[c * EVENT_EVERY]
-            head.replay()
-            ev0.record(stream)
-            back.replay()
-            ev1.record(stream)
+        for c in range(args.steps // GRAPH_STEPS):
+            graphs[c % len(graphs)].replay()
+    region[1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    com_ms = [ev0.elapsed_time(ev1) for ev0, ev1 in pairs.values()]
+    gpu_ms_per_step = region[0].elapsed_time(region[1]) / args.steps
 
-    # Per-kernel split: 10 eager steps after the timed region, every launch
+    # Roofline: ROOFLINE_STEPS eager steps after the timed region, the
+    # combine launch of each bound to its own event pair (a bound launch
+    # costs its step a few microseconds of host and queue time, which is why
+    # none sits inside the timed region).
+    rl_pairs = new_pairs(ROOFLINE_STEPS)
+    torch.cuda.synchronize()
+    for i in range(ROOFLINE_STEPS):
+        step(bufs[(args.steps + i) % sets], rl_pairs[i])
+    torch.cuda.synchronize()
+    com_ms = [a.elapsed_time(z) for a, z in rl_pairs]
+
+    # Per-kernel split: BREAKDOWN_STEPS eager steps after those, every launch
     # timed by its own bound events.
-    steps_taken = [breakdown_step(bufs[i % sets], new_pairs(16)) for i in range(10)]
+    steps_taken = [breakdown_step(bufs[i % sets], new_pairs(16))
+                   for i in range(BREAKDOWN_STEPS)]
     torch.cuda.synchronize()
     per_step = [split_kernels(t) for t in steps_taken]
     kern_ms = {r: [d[r] for d in per_step] for r in per_step[0] if r != "layout_launches"}
-    kern_ms["combine"] = com_ms
     mean = lambda v: sum(v) / len(v)
 
     def pct(v):
@@ -534,14 +532,25 @@ def main():
         raise SystemExit(f"layout status flags {status}: routing is invalid")
 
     combine_s = mean(com_ms) / 1e3
-    role_bytes = {"layout": nbytes["layout"], "dispatch": nbytes["dispatch"],
-                  "combine": nbytes["combine"],
-                  "layout+dispatch (fused)": nbytes["layout"] + nbytes["dispatch"]}
+    # When moe_dispatch_fused's layout launches read the token rows ahead,
+    # the dispatch's x reads happen in the layout's time, so the two are
+    # rated together: each rate below divides bytes by the time of the
+    # kernels that move them.
+    read_ahead = args.fused and "layout" in kern_ms
+    if read_ahead:
+        kern_ms["layout+dispatch"] = [a + b for a, b in zip(kern_ms["layout"],
+                                                            kern_ms["dispatch"])]
+    role_bytes = {"layout": nbytes["layout"], "combine": nbytes["combine"],
+                  "layout+dispatch (fused)": nbytes["layout"] + nbytes["dispatch"],
+                  "layout+dispatch": nbytes["layout"] + nbytes["dispatch"]}
+    if not read_ahead:
+        role_bytes["dispatch"] = nbytes["dispatch"]
     achieved = nbytes["combine"] / combine_s / 1e9
+    step_gbs = step_bytes / (ms_per_step / 1e3) / 1e9
     traffic = None if (fp8_combine or args.replicas > 0) else read_traffic(w.name)
     result = {
         "metric": METRIC,
-        "value": round(step_bytes / (ms_per_step / 1e3) / 1e9, 2),
+        "value": round(step_gbs, 2),
         "unit": "GB/s",
         "tokens_per_s": round(w.bs / (ms_per_step / 1e3), 1),
         "n_gpus": 1,
@@ -562,7 +571,7 @@ def main():
                                                            if w.routing == "zipf" else ""),
                    "align": w.align, "capacity_rows": cap, "buffer_sets": sets,
                    "x_bytes_between_reuse": 2 * w.bs * w.hidden * (sets - 1),
-                   "launch": (f"hip graphs of {EVENT_EVERY} steps" if args.graph else "eager"),
+                   "launch": (f"hip graphs of {GRAPH_STEPS} steps" if args.graph else "eager"),
                    "layout_dispatch": (("moe_dispatch_fused_replicated" if args.replicas > 0
                                         else "moe_dispatch_fused") if args.fused
                                        else "separate"),
@@ -571,23 +580,29 @@ def main():
                                  "physical": n_phys} if args.replicas > 0 else None),
                    "ep_world_size": args.ep or None,
                    "bytes_per_step": step_bytes},
-        "kernel_times": ("combine: timed region; layout and dispatch: 10 eager steps after "
-                         "it, events bound to each kernel launch"),
+        "gpu_ms_per_step": round(gpu_ms_per_step, 4),
+        "kernel_times": (f"events bound to each launch (kernel start to end), after the timed "
+                         f"region: the combine in {ROOFLINE_STEPS} steps, every kernel in "
+                         f"{BREAKDOWN_STEPS} steps after those"),
         "layout_launches": per_step[0].get("layout_launches", 0),
         "kernels_ms": {r: round(mean(v), 4) for r, v in kern_ms.items()},
-        "kernels_gbs": {r: round(role_bytes[r] / mean(v) / 1e6, 1) for r, v in kern_ms.items()},
+        "kernels_gbs": {r: round(role_bytes[r] / mean(v) / 1e6, 1) for r, v in kern_ms.items()
+                        if r in role_bytes},
         "kernels_us_p10_p50_p90": {r: pct(v) for r, v in kern_ms.items()},
         "roofline": {"kernel": "combine_fp8" if fp8_combine else "combine", "bound": "hbm",
                      "timed_launches": len(com_ms),
-                     "timing": ("HIP events on the launch stream around the graph replay "
-                                "holding the combine" if graphs is not None else
-                                "HIP events bound to the combine launch (kernel start to end)"),
+                     "timing": (f"HIP events bound to the combine launch (kernel start to end) "
+                                f"in {ROOFLINE_STEPS} eager steps after the timed region"),
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
-                     "algorithmic_bytes_per_launch": nbytes["combine"]},
+                     "algorithmic_bytes_per_launch": nbytes["combine"],
+                     "us_p10_p50_p90": pct(com_ms),
+                     "breakdown_combine_us": round(mean(kern_ms["combine"]) * 1e3, 2),
+                     "step_achieved": round(step_gbs, 1),
+                     "step_frac": round(step_gbs / HBM_PEAK_GBS, 4)},
     }
     # The probe models bf16 rows at bandwidth-bound sizes (a decode-sized
     # step is launch-latency bound, and a probe of it says nothing).

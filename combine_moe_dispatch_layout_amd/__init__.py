@@ -194,7 +194,7 @@ def moe_dispatch_layout(expert_ids: torch.Tensor, num_experts: int, align: int =
                      torch.empty(1, dtype=torch.int32, device=dev))
     ws_bytes = moe_dispatch_layout_workspace_size(bs, k, num_experts)
     if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     rc = load_library().moe_dispatch_layout(
         _ptr(expert_ids), bs, k, num_experts, align, _ptr(out.expert_counts),
         _ptr(out.ep_send_counts), _ptr(out.expand_idx), _ptr(out.status), _ptr(workspace),
@@ -273,7 +273,7 @@ def moe_dispatch_fused(x: torch.Tensor, expert_ids: torch.Tensor, num_experts: i
                                    device=dev)
     ws_bytes = moe_dispatch_layout_workspace_size(bs, k, num_experts)
     if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     rc = load_library().moe_dispatch_fused(
         _ptr(x), _row_stride(x, "x"), bs, hidden, _ptr(expert_ids), k, num_experts, align,
         _ptr(out.expert_counts), _ptr(out.ep_send_counts), _ptr(out.expand_idx),
@@ -372,7 +372,7 @@ def moe_dispatch_layout_replicated(expert_ids: torch.Tensor, num_experts: int,
         replica_ids = torch.empty((bs, k), dtype=torch.int32, device=dev)
     ws_bytes = moe_dispatch_layout_workspace_size(bs, k, p)
     if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     rc = load_library().moe_dispatch_layout_replicated(
         _ptr(expert_ids), bs, k, num_experts, _ptr(replica_offsets), _ptr(replica_thresholds), p,
         seed & 0xFFFFFFFFFFFFFFFF, align, _ptr(replica_ids), _ptr(out.expert_counts),
@@ -427,7 +427,7 @@ def moe_dispatch_fused_replicated(x: torch.Tensor, expert_ids: torch.Tensor, num
                                    device=dev)
     ws_bytes = moe_dispatch_layout_workspace_size(bs, k, p)
     if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     rc = load_library().moe_dispatch_fused_replicated(
         _ptr(x), _row_stride(x, "x"), bs, hidden, _ptr(expert_ids), k, num_experts,
         _ptr(replica_offsets), _ptr(replica_thresholds), p, seed & 0xFFFFFFFFFFFFFFFF, align,
@@ -461,7 +461,7 @@ def moe_dispatch_layout_ep(expert_ids: torch.Tensor, num_experts: int, ep_world_
         rank_offsets = torch.empty(max(ep_world_size, 0) + 1, dtype=torch.int32, device=dev)
     ws_bytes = moe_dispatch_layout_workspace_size(bs, k, num_experts)
     if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     rc = load_library().moe_dispatch_layout_ep(
         _ptr(expert_ids), bs, k, num_experts, ep_world_size, align, _ptr(out.expert_counts),
         _ptr(out.ep_send_counts), _ptr(rank_offsets), _ptr(out.expand_idx), _ptr(out.status),

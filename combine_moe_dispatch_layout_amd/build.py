@@ -40,9 +40,14 @@ def _obj_dir() -> str:
     return d
 
 
+# Build-time tuning macros (for example "-DMOE_FUSED_DEFER=0"); the
+# defaults in csrc/moe_internal.h are the measured choices.
+EXTRA = os.environ.get("MOE_HIPCC_DEFINES", "").split()
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(_obj_dir(), os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, f"-I{INCLUDE}", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA, f"-I{INCLUDE}", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -22,7 +22,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool is_pow2(int32_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
@@ -80,11 +80,14 @@ int scatter_args_check(const void* x, int64_t x_stride, int32_t hidden, const vo
   return MOE_OK;
 }
 
-// The layout launch(es) over `ranked` experts (through the replica map when
-// it has one), then the scatter of x by `route_ids` (the ids the layout
-// ranked: expert_ids, or the replica ids it writes), on one stream.  The
-// layout launches read contiguous token rows ahead (at most
-// kReadAheadMaxBytes); when every row was read, the bf16 scatter takes its
+// The layout over `ranked` experts (through the replica map when it has
+// one), then the scatter of x by `route_ids` (the ids the layout ranked:
+// expert_ids, or the replica ids it writes), on one stream.  With several
+// ranking workgroups this is two launches: the ranking launch, whose last
+// workgroup also scans the histograms and whose spare workgroups read
+// contiguous token rows ahead (at most kReadAheadMaxBytes), and the
+// scatter, which adds each token's workgroup prefix to its ranks and writes
+// expand_idx.  When every row was read ahead, the bf16 scatter takes its
 // cache-resident launch shape.
 int layout_then_scatter(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
                         const int32_t* expert_ids, const int32_t* route_ids, int32_t k,
@@ -106,17 +109,27 @@ int layout_then_scatter(const void* x, int64_t x_stride, int32_t bs, int32_t hid
     ahead.split = ahead.vecs * moe::kReadAheadRankPercent / 100;
     rows_cached = ahead.vecs == vecs && moe::read_ahead_runs(plan, ahead);
   }
+  const bool defer = moe::kFusedDefer && plan.blocks > 1;
   hipError_t err = moe::launch_layout(expert_ids, k, ranked, align, plan, counts, send,
                                       expand_idx, status, workspace, map, moe::RankSplit{}, s,
-                                      ahead);
+                                      ahead, defer);
   if (err != hipSuccess || bs == 0) return hip_status(err);
+  moe::DeferredRanks dr;
+  const int32_t* ranks = expand_idx;
+  if (defer) {
+    const moe::LayoutScratch ws = moe::layout_scratch(plan, ranked, workspace);
+    dr.base = ws.hist;
+    dr.tokens_per_block = (int32_t)(plan.pairs_per_block / k);
+    dr.expand_idx = expand_idx;
+    ranks = ws.ranks;
+  }
   if (out_dtype == MOE_BF16)
-    return hip_status(moe::launch_dispatch_bf16(x, x_stride, bs, hidden, route_ids, expand_idx,
-                                                send, k, ranked, expand_x, expand_x_stride,
-                                                capacity_rows, status, s, rows_cached));
-  return hip_status(moe::launch_dispatch_fp8(x, x_stride, bs, hidden, route_ids, expand_idx,
-                                             send, k, ranked, expand_x, expand_x_stride,
-                                             capacity_rows, quant_scales, status, s));
+    return hip_status(moe::launch_dispatch_bf16(x, x_stride, bs, hidden, route_ids, ranks, send,
+                                                k, ranked, expand_x, expand_x_stride,
+                                                capacity_rows, status, s, rows_cached, dr));
+  return hip_status(moe::launch_dispatch_fp8(x, x_stride, bs, hidden, route_ids, ranks, send, k,
+                                             ranked, expand_x, expand_x_stride, capacity_rows,
+                                             quant_scales, status, s, dr));
 }
 
 }  // namespace

@@ -21,26 +21,34 @@ template <int THREADS, int VPT, int KMAX>
 __global__ __launch_bounds__(THREADS) void combine_kernel(
     const u32x4* __restrict__ y, int64_t ys, int64_t cap, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ send,
-    const float* __restrict__ scales, const u32x4* __restrict__ shared, int64_t ss,
+    const float* __restrict__ scales, const u32x4* shared, int64_t ss,
     int32_t nvec, int32_t nchunks, int32_t k, int32_t E,
     u32x4* __restrict__ out, int32_t* status) {
-  __shared__ int send_lds[kMaxExperts + 1];
+  __shared__ int send_lds[StagedSend<THREADS>::kSlots];
   const int32_t t = blockIdx.x / nchunks;
   const int32_t chunk = blockIdx.x - t * nchunks;
   PairMeta meta;
   fetch_pair_meta(meta, t, k, ids, idx, scales);
+  StagedSend<THREADS> staged;
+  staged.load(send, E + 1);
+  // The shared row does not depend on the routes: its loads go out now, but
+  // after the send counts, so the routes need not wait for them.
+  // Every lane loads (a lane past the row end repeats its last vector, and
+  // without a shared row all lanes read a zero vector), so no branch
+  // separates these loads from the send counts' loads.
   const int32_t v0 = chunk * (THREADS * VPT) + threadIdx.x;
   u32x4 sv[VPT];
 #pragma unroll
   for (int jv = 0; jv < VPT; ++jv) {
-    const int32_t v = v0 + jv * THREADS;
-    sv[jv] = u32x4{0u, 0u, 0u, 0u};
-    if (shared && v < nvec) sv[jv] = load_stream(shared + (int64_t)t * ss + v);
+    const int32_t v = min(v0 + jv * THREADS, nvec - 1);
+    sv[jv] = load_stream(shared ? shared + (int64_t)t * ss + v : &kZeroVec);
   }
-  stage_send(send_lds, send, E);  // overlaps the fetches above
+  keep_order();
+  staged.store(send_lds);
+  __syncthreads();
   int64_t slot[KMAX];
   float w[KMAX];
-  resolve_routes<KMAX>(meta, send_lds, k, E, cap, slot, w, status,
+  resolve_routes<KMAX>(meta, send_lds, nullptr, k, E, cap, slot, w, status,
                        threadIdx.x < kWave && chunk == 0);
 
   u32x4 yv[VPT][KMAX];
@@ -112,10 +120,10 @@ __global__ __launch_bounds__(1024) void combine_fp8_kernel(
     sh0 = load_stream(shared + (int64_t)t * ss + 2 * g);
     sh1 = load_stream(shared + (int64_t)t * ss + 2 * g + 1);
   }
-  stage_send(send_lds, send, E);  // overlaps the fetches above
+  stage_send_any(send_lds, send, E);  // overlaps the fetches above
   int64_t slot[KMAX];
   float w[KMAX];
-  resolve_routes<KMAX>(meta, send_lds, k, E, cap, slot, w, status,
+  resolve_routes<KMAX>(meta, send_lds, nullptr, k, E, cap, slot, w, status,
                        threadIdx.x < kWave && chunk == 0);
 
   if (g >= ngroups) return;  // no workgroup barrier follows

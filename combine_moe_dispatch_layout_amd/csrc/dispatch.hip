@@ -14,32 +14,73 @@
 namespace moe {
 namespace {
 
-// LDS_INTS sizes the send-count array; a larger array than the counts need
-// only serves to cap how many workgroups share a compute unit.
-template <int THREADS, int VPT, int KMAX, int LDS_INTS>
+// The routes' offset tables, staged in LDS in two steps (load, then store)
+// around the row loads: the send counts, and with deferred ranks also the
+// column prefix of the ranking workgroup that holds token t (kBase ints
+// into the LDS area, which holds at least kInts ints).
+template <int THREADS, bool DEFER>
+struct RouteTables {
+  using Send = StagedSend<THREADS>;
+  using Base = StagedInts<THREADS, (DEFER ? kMaxExperts : 1)>;
+  static constexpr int kBase = Send::kSlots;
+  static constexpr int kInts = Send::kSlots + (DEFER ? Base::kSlots : 0);
+  Send send;
+  Base base;
+  __device__ __forceinline__ void load(const int32_t* __restrict__ send_counts,
+                                       const DeferredRanks& dr, int32_t t, int32_t E) {
+    send.load(send_counts, E + 1);
+    if (DEFER) base.load(dr.base + (int64_t)(t / dr.tokens_per_block) * E, E);
+  }
+  // Writes the tables and synchronises; returns the column prefix table
+  // (nullptr without deferred ranks).
+  __device__ __forceinline__ const int* store(int* lds) const {
+    send.store(lds);
+    if (DEFER) base.store(lds + kBase);
+    __syncthreads();
+    return DEFER ? lds + kBase : nullptr;
+  }
+};
+
+// With deferred ranks, the first-chunk workgroup of token t writes the
+// token's final expand_idx (rank within the workgroup + column prefix).
+template <bool DEFER>
+__device__ __forceinline__ void write_deferred(const PairMeta& m, const int* base_lds,
+                                               const DeferredRanks& dr, int32_t t, int32_t k,
+                                               int32_t E, bool first_chunk) {
+  if (!DEFER || !first_chunk || threadIdx.x >= (unsigned)k) return;
+  const bool ok = m.r >= 0 && m.e >= 0 && m.e < E;
+  dr.expand_idx[(int64_t)t * k + threadIdx.x] = ok ? base_lds[m.e] + m.r : -1;
+}
+
+// LDS_INTS sizes the offset tables; a larger array than they need only
+// serves to cap how many workgroups share a compute unit.
+template <int THREADS, int VPT, int KMAX, int LDS_INTS, bool DEFER>
 __global__ __launch_bounds__(THREADS) void dispatch_bf16_kernel(
-    const u32x4* __restrict__ x, int64_t xs, int32_t nvec, int32_t nchunks,
+    const u32x4* x, int64_t xs, int32_t nvec, int32_t nchunks,
     const int32_t* __restrict__ ids, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ send, int32_t k, int32_t E, u32x4* __restrict__ out, int64_t os,
-    int64_t cap, int32_t* status) {
-  static_assert(LDS_INTS >= kMaxExperts + 1, "send counts must fit");
-  __shared__ int send_lds[LDS_INTS];
+    int64_t cap, int32_t* status, DeferredRanks dr) {
+  static_assert(LDS_INTS >= RouteTables<THREADS, DEFER>::kInts, "tables must fit");
+  __shared__ int lds[LDS_INTS];
   const int32_t t = blockIdx.x / nchunks;
   const int32_t chunk = blockIdx.x - t * nchunks;
   PairMeta meta;
   fetch_pair_meta(meta, t, k, ids, idx, nullptr);
+  RouteTables<THREADS, DEFER> tables;
+  tables.load(send, dr, t, E);
+  // The row loads go out after the tables' loads, so the routes need not
+  // wait for them.
+  // (A lane past the row end repeats the last vector and stores nothing.)
   const int32_t v0 = chunk * (THREADS * VPT) + threadIdx.x;
   const u32x4* src = x + (int64_t)t * xs;
   u32x4 r[VPT];
 #pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    const int32_t v = v0 + j * THREADS;
-    if (v < nvec) r[j] = src[v];
-  }
-  stage_send(send_lds, send, E);  // overlaps the loads above
+  for (int j = 0; j < VPT; ++j) r[j] = src[min(v0 + j * THREADS, nvec - 1)];
+  keep_order();
+  const int* base_lds = tables.store(lds);
   int64_t slot[KMAX];
   float unused_w[KMAX];
-  resolve_routes<KMAX>(meta, send_lds, k, E, cap, slot, unused_w, status,
+  resolve_routes<KMAX>(meta, lds, base_lds, k, E, cap, slot, unused_w, status,
                        threadIdx.x < kWave && chunk == 0);
 #pragma unroll
   for (int jj = 0; jj < KMAX; ++jj) {
@@ -51,35 +92,41 @@ __global__ __launch_bounds__(THREADS) void dispatch_bf16_kernel(
       if (v < nvec) store_stream(r[j], dst + v);
     }
   }
+  write_deferred<DEFER>(meta, base_lds, dr, t, k, E, chunk == 0);
 }
 
 // Each thread owns 16 consecutive channels (two 16-byte loads of bf16, one
 // 16-byte store of e4m3 codes); 8 neighbouring lanes form one 128-channel
 // scale block and combine their maxima with cross-lane exchanges.
-template <int THREADS, int KMAX>
+template <int THREADS, int KMAX, bool DEFER>
 __global__ __launch_bounds__(THREADS) void dispatch_fp8_kernel(
-    const u32x4* __restrict__ x, int64_t xs, int32_t ngroups, int32_t nchunks,
+    const u32x4* x, int64_t xs, int32_t ngroups, int32_t nchunks,
     const int32_t* __restrict__ ids, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ send, int32_t k, int32_t E, u32x4* __restrict__ out, int64_t os,
-    float* __restrict__ scales, int32_t nblk, int64_t cap, int32_t* status) {
-  __shared__ int send_lds[kMaxExperts + 1];
+    float* __restrict__ scales, int32_t nblk, int64_t cap, int32_t* status, DeferredRanks dr) {
+  __shared__ int lds[RouteTables<THREADS, DEFER>::kInts];
   const int32_t t = blockIdx.x / nchunks;
   const int32_t chunk = blockIdx.x - t * nchunks;
   PairMeta meta;
   fetch_pair_meta(meta, t, k, ids, idx, nullptr);
 
+  RouteTables<THREADS, DEFER> tables;
+  tables.load(send, dr, t, E);
   const int32_t g = chunk * THREADS + threadIdx.x;  // 16-channel group within the row
   const bool active = g < ngroups;
-  u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-  if (active) {
-    const u32x4* src = x + (int64_t)t * xs + 2 * (int64_t)g;
+  u32x4 a, b;
+  {
+    // A lane past the row end loads the row's last group (and takes zeros).
+    const u32x4* src = x + (int64_t)t * xs + 2 * (int64_t)min(g, ngroups - 1);
     a = src[0];
     b = src[1];
   }
-  stage_send(send_lds, send, E);  // overlaps the loads above
+  keep_order();
+  const int* base_lds = tables.store(lds);
+  if (!active) a = b = u32x4{0u, 0u, 0u, 0u};
   int64_t slot[KMAX];
   float unused_w[KMAX];
-  resolve_routes<KMAX>(meta, send_lds, k, E, cap, slot, unused_w, status,
+  resolve_routes<KMAX>(meta, lds, base_lds, k, E, cap, slot, unused_w, status,
                        threadIdx.x < kWave && chunk == 0);
 
   float s;
@@ -98,6 +145,7 @@ __global__ __launch_bounds__(THREADS) void dispatch_fp8_kernel(
     if (active) store_stream(codes, out + slot[jj] * os + g);
     if (writes_scale) scales[slot[jj] * nblk + (g >> 3)] = s;
   }
+  write_deferred<DEFER>(meta, base_lds, dr, t, k, E, chunk == 0);
 }
 
 int kmax_for(int32_t k) { return k <= 2 ? 2 : k <= 4 ? 4 : k <= 8 ? 8 : 16; }
@@ -110,12 +158,12 @@ int kmax_for(int32_t k) { return k <= 2 ? 2 : k <= 4 ? 4 : k <= 8 ? 8 : 16; }
 // unit (2 waves per SIMD).  Rows that still come from HBM need the latency
 // hiding of full occupancy, so they keep 128-thread workgroups with only
 // the send counts in LDS.
-template <int THREADS, int LDS_INTS>
+template <int THREADS, int LDS_INTS, bool DEFER>
 hipError_t launch_bf16_shape(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
                              const int32_t* ids, const int32_t* expand_idx, const int32_t* send,
                              int32_t k, int32_t num_experts, void* expand_x,
                              int64_t expand_x_stride, int64_t capacity_rows, int32_t* status,
-                             hipStream_t stream) {
+                             hipStream_t stream, const DeferredRanks& dr) {
   constexpr int kVpt = MOE_DISPATCH_VPT;
   const int32_t nvec = hidden / 8;  // 16-byte vectors per row
   const int32_t nchunks = (nvec + THREADS * kVpt - 1) / (THREADS * kVpt);
@@ -126,24 +174,64 @@ hipError_t launch_bf16_shape(const void* x, int64_t x_stride, int32_t bs, int32_
   const int64_t xs = x_stride / 8, os = expand_x_stride / 8;
   switch (kmax_for(k)) {
     case 2:
-      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 2, LDS_INTS>, grid, THREADS, stream,
-          xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          capacity_rows, status);
+      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 2, LDS_INTS, DEFER>, grid, THREADS,
+          stream, xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
+          capacity_rows, status, dr);
       break;
     case 4:
-      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 4, LDS_INTS>, grid, THREADS, stream,
-          xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          capacity_rows, status);
+      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 4, LDS_INTS, DEFER>, grid, THREADS,
+          stream, xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
+          capacity_rows, status, dr);
       break;
     case 8:
-      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 8, LDS_INTS>, grid, THREADS, stream,
-          xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          capacity_rows, status);
+      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 8, LDS_INTS, DEFER>, grid, THREADS,
+          stream, xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
+          capacity_rows, status, dr);
       break;
     default:
-      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 16, LDS_INTS>, grid, THREADS, stream,
-          xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          capacity_rows, status);
+      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 16, LDS_INTS, DEFER>, grid, THREADS,
+          stream, xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
+          capacity_rows, status, dr);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <bool DEFER>
+hipError_t launch_fp8_shape(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
+                            const int32_t* ids, const int32_t* expand_idx, const int32_t* send,
+                            int32_t k, int32_t num_experts, void* expand_x,
+                            int64_t expand_x_stride, int64_t capacity_rows, float* quant_scales,
+                            int32_t* status, hipStream_t stream, const DeferredRanks& dr) {
+  constexpr int kThreads = MOE_FP8_THREADS;
+  const int32_t ngroups = hidden / 16;
+  const int32_t nchunks = (ngroups + kThreads - 1) / kThreads;
+  const int32_t n_items = bs * nchunks;
+  const dim3 grid((uint32_t)n_items);
+  const u32x4* xv = static_cast<const u32x4*>(x);
+  u32x4* ov = static_cast<u32x4*>(expand_x);
+  const int64_t xs = x_stride / 8, os = expand_x_stride / 16;
+  const int32_t nblk = hidden / 128;
+  switch (kmax_for(k)) {
+    case 2:
+      launch_kernel(dispatch_fp8_kernel<kThreads, 2, DEFER>, grid, kThreads, stream,
+          xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
+          quant_scales, nblk, capacity_rows, status, dr);
+      break;
+    case 4:
+      launch_kernel(dispatch_fp8_kernel<kThreads, 4, DEFER>, grid, kThreads, stream,
+          xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
+          quant_scales, nblk, capacity_rows, status, dr);
+      break;
+    case 8:
+      launch_kernel(dispatch_fp8_kernel<kThreads, 8, DEFER>, grid, kThreads, stream,
+          xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
+          quant_scales, nblk, capacity_rows, status, dr);
+      break;
+    default:
+      launch_kernel(dispatch_fp8_kernel<kThreads, 16, DEFER>, grid, kThreads, stream,
+          xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
+          quant_scales, nblk, capacity_rows, status, dr);
       break;
   }
   return hipGetLastError();
@@ -158,53 +246,38 @@ hipError_t launch_dispatch_bf16(const void* x, int64_t x_stride, int32_t bs, int
                                 const int32_t* ids, const int32_t* expand_idx,
                                 const int32_t* send, int32_t k, int32_t num_experts,
                                 void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
-                                int32_t* status, hipStream_t stream, bool rows_cached) {
-  if (rows_cached)
-    return launch_bf16_shape<kCachedRowsThreads, kCachedRowsLdsInts>(
+                                int32_t* status, hipStream_t stream, bool rows_cached,
+                                const DeferredRanks& dr) {
+  if (rows_cached && dr.base)
+    return launch_bf16_shape<kCachedRowsThreads, kCachedRowsLdsInts, true>(
         x, x_stride, bs, hidden, ids, expand_idx, send, k, num_experts, expand_x,
-        expand_x_stride, capacity_rows, status, stream);
-  return launch_bf16_shape<MOE_DISPATCH_THREADS, kMaxExperts + 1>(
+        expand_x_stride, capacity_rows, status, stream, dr);
+  if (rows_cached)
+    return launch_bf16_shape<kCachedRowsThreads, kCachedRowsLdsInts, false>(
+        x, x_stride, bs, hidden, ids, expand_idx, send, k, num_experts, expand_x,
+        expand_x_stride, capacity_rows, status, stream, dr);
+  if (dr.base)
+    return launch_bf16_shape<MOE_DISPATCH_THREADS, RouteTables<MOE_DISPATCH_THREADS, true>::kInts, true>(
+        x, x_stride, bs, hidden, ids, expand_idx, send, k, num_experts, expand_x,
+        expand_x_stride, capacity_rows, status, stream, dr);
+  return launch_bf16_shape<MOE_DISPATCH_THREADS, RouteTables<MOE_DISPATCH_THREADS, false>::kInts, false>(
       x, x_stride, bs, hidden, ids, expand_idx, send, k, num_experts, expand_x,
-      expand_x_stride, capacity_rows, status, stream);
+      expand_x_stride, capacity_rows, status, stream, dr);
 }
 
 hipError_t launch_dispatch_fp8(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
                                const int32_t* ids, const int32_t* expand_idx,
                                const int32_t* send, int32_t k, int32_t num_experts,
                                void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
-                               float* quant_scales, int32_t* status, hipStream_t stream) {
-  constexpr int kThreads = MOE_FP8_THREADS;
-  const int32_t ngroups = hidden / 16;
-  const int32_t nchunks = (ngroups + kThreads - 1) / kThreads;
-  const int32_t n_items = bs * nchunks;
-  const dim3 grid((uint32_t)n_items);
-  const u32x4* xv = static_cast<const u32x4*>(x);
-  u32x4* ov = static_cast<u32x4*>(expand_x);
-  const int64_t xs = x_stride / 8, os = expand_x_stride / 16;
-  const int32_t nblk = hidden / 128;
-  switch (kmax_for(k)) {
-    case 2:
-      launch_kernel(dispatch_fp8_kernel<kThreads, 2>, grid, kThreads, stream,
-          xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          quant_scales, nblk, capacity_rows, status);
-      break;
-    case 4:
-      launch_kernel(dispatch_fp8_kernel<kThreads, 4>, grid, kThreads, stream,
-          xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          quant_scales, nblk, capacity_rows, status);
-      break;
-    case 8:
-      launch_kernel(dispatch_fp8_kernel<kThreads, 8>, grid, kThreads, stream,
-          xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          quant_scales, nblk, capacity_rows, status);
-      break;
-    default:
-      launch_kernel(dispatch_fp8_kernel<kThreads, 16>, grid, kThreads, stream,
-          xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          quant_scales, nblk, capacity_rows, status);
-      break;
-  }
-  return hipGetLastError();
+                               float* quant_scales, int32_t* status, hipStream_t stream,
+                               const DeferredRanks& dr) {
+  if (dr.base)
+    return launch_fp8_shape<true>(x, x_stride, bs, hidden, ids, expand_idx, send, k,
+                                  num_experts, expand_x, expand_x_stride, capacity_rows,
+                                  quant_scales, status, stream, dr);
+  return launch_fp8_shape<false>(x, x_stride, bs, hidden, ids, expand_idx, send, k, num_experts,
+                                 expand_x, expand_x_stride, capacity_rows, quant_scales, status,
+                                 stream, dr);
 }
 
 }  // namespace moe

@@ -3,10 +3,12 @@
 // ep_send_counts triple of the npu_moe_distribute_combine page; the padding
 // is the grouped GEMM's 128-row M-tile from the TEMPO summary, section 1).
 //
-// Ranking pass (one or more workgroups of 8 waves):
-//   Wave w of a workgroup owns a contiguous run of 64*R pairs and walks it in
-//   R sub-rounds of 64 (one pair per lane), entirely against its own LDS
-//   slice, so no workgroup barrier is needed inside the walk:
+// Ranking pass (one or more workgroups of 8 waves, at most kLayoutMaxBlocks):
+//   A workgroup owns a contiguous range of whole tokens and walks it in
+//   chunks of at most 2048 pairs.  Within a chunk, wave w owns a contiguous
+//   run of 64*R pairs and walks it in R sub-rounds of 64 (one pair per lane),
+//   entirely against its own LDS slice, so no workgroup barrier is needed
+//   inside the walk:
 //     - every lane ORs its bit into mask[w][e] for its expert e (LDS atomic
 //       OR: the result does not depend on the order the lanes arrive in);
 //     - a lane's local rank = wave_run[w][e] (pairs of e in this wave's
@@ -14,18 +16,25 @@
 //     - the lowest lane of each expert group advances wave_run[w][e] and
 //       clears the mask word.
 //   LDS instructions of one wave execute in issue order, so each step sees
-//   the previous one.  After one workgroup barrier a per-expert exclusive
-//   prefix over the 8 waves turns local ranks into workgroup ranks.  Nothing
-//   positional is decided by an atomic race, so the layout is deterministic.
+//   the previous one.  After a workgroup barrier a per-expert exclusive
+//   prefix over the 8 waves, started from the counts of the workgroup's
+//   earlier chunks, turns local ranks into ranks within the workgroup.
+//   Nothing positional is decided by an atomic race, so the layout is
+//   deterministic.
 // Repeated ids: each thread checks one token's K ids against each other in
 //   registers.
 // Single workgroup (<= 2048 pairs): the same kernel also writes the counts and
 //   the padded exclusive scan, so small batches take one launch.
-// Several workgroups: each writes its expert histogram to the workspace; a
-//   second launch gives every workgroup the column sum of the histograms of
-//   the workgroups before it (its base per expert), adds that base to its
-//   ranks, and the last workgroup (which needs every row anyway) writes the
-//   counts, the padded scan and the status word.
+// Several workgroups: each writes its expert histogram to the workspace,
+//   publishes it (device-scope fence) and counts itself in on an arrival
+//   counter.  The workgroup that arrives last sees every histogram: it turns
+//   the histograms, in place, into the exclusive prefix over workgroups of
+//   each expert's column (the device-wide scan, each column scanned once),
+//   writes the counts, the padded scan and the status word, and sets the
+//   counter back to zero for the next call.  Nobody waits for anybody.  The
+//   ranks then need their workgroup's column prefix added: by a second, short
+//   launch (moe_dispatch_layout), or by the scatter itself when the layout is
+//   followed by one (moe_dispatch_fused).
 #include "moe_internal.h"
 
 namespace moe {
@@ -79,9 +88,9 @@ __device__ void write_counts_and_offsets(int c, int32_t E, int32_t align, int* w
 // Flags an expert (an id in [0, E)) repeated within one of the tokens whose
 // first pair lies in [begin, end).
 __device__ __forceinline__ int duplicate_flags(const int32_t* __restrict__ ids, int32_t k,
-                                               int32_t E, int begin, int end) {
+                                               int32_t E, int64_t begin, int64_t end) {
   int fl = 0;
-  for (int t = (begin + k - 1) / k + (int)threadIdx.x; t * k < end; t += kLayoutThreads) {
+  for (int64_t t = (begin + k - 1) / k + (int)threadIdx.x; t * k < end; t += kLayoutThreads) {
     int v[kMaxTopK];
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) v[j] = (j < k) ? ids[t * k + j] : -1 - j;
@@ -104,219 +113,290 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t i) {
   return z ^ (z >> 31);
 }
 
+// Run by the workgroup that arrived last, after its acquire fence: every
+// workgroup's histogram row is in ws.hist[b*E + e].  Each expert's column
+// is scanned once, in place, into the exclusive prefix over workgroups
+// (workgroup b's first rank for that expert); its total is the expert's
+// count, from which the padded scan follows.  `part` is LDS scratch of at
+// least kLayoutThreads ints.
+__device__ void finish_layout(const LayoutScratch& ws, int32_t blocks, int32_t E, int32_t align,
+                              int* part, int* wave_tot, int* flags_lds,
+                              int32_t* __restrict__ counts, int32_t* __restrict__ send,
+                              int32_t* __restrict__ status, const RankSplit& ranks) {
+  const int tid = threadIdx.x;
+  int epad = 1;
+  while (epad < E) epad <<= 1;
+  const int groups = kLayoutThreads / epad;  // threads per column, each a run of rows
+  const int col = tid & (epad - 1);
+  const int grp = tid / epad;
+  const int rows = (blocks + groups - 1) / groups;
+  const int r0 = min(blocks, grp * rows), r1 = min(blocks, r0 + rows);
+  const bool active = col < E;
+  int32_t* __restrict__ h = ws.hist;
+
+  // Pass 1: this thread's partial column sum, 16 independent loads at a time.
+  int partial = 0;
+  if (active) {
+    for (int b0 = r0; b0 < r1; b0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        v[u] = (b0 + u < r1) ? h[(int64_t)(b0 + u) * E + col] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) partial += v[u];
+    }
+  }
+  part[tid] = partial;
+  int f = 0;
+  for (int b = tid; b < blocks; b += kLayoutThreads) f |= ws.flags[b];
+  if (f) atomicOr(flags_lds, f);
+  __syncthreads();
+  int run = 0, total = 0;
+  for (int g = 0; g < groups; ++g) {
+    const int p = part[g * epad + col];
+    run += (g < grp) ? p : 0;
+    total += p;
+  }
+  // Pass 2: the exclusive prefix down the column, written over the counts.
+  if (active) {
+    for (int b0 = r0; b0 < r1; b0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        v[u] = (b0 + u < r1) ? h[(int64_t)(b0 + u) * E + col] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (b0 + u < r1) h[(int64_t)(b0 + u) * E + col] = run;
+        run += v[u];
+      }
+    }
+  }
+  __syncthreads();
+  if (grp == 0) part[col] = total;  // column totals (partial sums no longer needed)
+  __syncthreads();
+  write_counts_and_offsets(tid < E ? part[tid] : 0, E, align, wave_tot, counts, send, ranks);
+  if (tid == 0) {
+    if (status) *status = *flags_lds;
+    atomicExch(ws.arrivals, 0);  // ready for the next call
+  }
+}
+
 // Ranking over E "experts".  With a replica map, ids are logical experts in
 // [0, map.n_logical) and each pair is first sent to one of its expert's
 // physical replicas (E = number of replicas): u = upper 32 bits of the pair's
 // SplitMix64 draw, replica = first r of the expert's range with
 // u <= thresholds[r] (TEMPO summary, section 2: probabilistic replica
 // dispatch and count gathering in one in-graph kernel).
+// Workgroups past rank_blocks read the token rows ahead instead.
 template <int R>
 __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     const int32_t* __restrict__ ids, int32_t n_pairs, int32_t k, int32_t E, int32_t align,
-    int32_t* __restrict__ expand_idx, int32_t* __restrict__ block_hist,
-    int32_t* __restrict__ block_flags, int32_t* __restrict__ counts, int32_t* __restrict__ send,
-    int32_t* __restrict__ status, ReplicaMap map, RankSplit ranks, ReadAhead ahead,
-    int32_t rank_blocks, int32_t ahead_blocks) {
-  if ((int32_t)blockIdx.x >= rank_blocks) {  // read-ahead workgroup: vectors [0, split)
+    int32_t chunk_pairs, int32_t chunks, int32_t* __restrict__ ranks_out, LayoutScratch ws,
+    int32_t* __restrict__ counts, int32_t* __restrict__ send, int32_t* __restrict__ status,
+    ReplicaMap map, RankSplit ranks, ReadAhead ahead, int32_t rank_blocks,
+    int32_t ahead_blocks) {
+  if ((int32_t)blockIdx.x >= rank_blocks) {
     read_ahead(ahead, rank_blocks, ahead_blocks, 0, ahead.split);
     return;
   }
   __shared__ unsigned long long mask[kLayoutWaves][kMaxExperts];  // 32 KB
   __shared__ int wave_run[kLayoutWaves][kMaxExperts];             // 16 KB
+  __shared__ int blk_run[kMaxExperts];   // pairs per expert in earlier chunks
   __shared__ int rep_off[kMaxExperts + 1];
   __shared__ uint32_t rep_thr[kMaxExperts];
   __shared__ int wave_tot[kLayoutWaves];
   __shared__ int flags_lds;
+  __shared__ int last_lds;
   const bool mapped = map.offsets != nullptr;
   const int32_t n_ids = mapped ? map.n_logical : E;  // valid range of the input ids
 
-  constexpr int kPairs = kLayoutThreads * R;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int begin = blockIdx.x * kPairs;
-  const int end = min(n_pairs, begin + kPairs);
-  const int wbase = begin + wave * (kWave * R);
+  const int64_t ppb = (int64_t)chunk_pairs * chunks;
+  const int64_t bbegin = (int64_t)blockIdx.x * ppb;
+  const int64_t bend = min((int64_t)n_pairs, bbegin + ppb);
 
-  // All id loads of this thread first.
+  // The first chunk's id loads are issued before the LDS set-up.
   int e[R];
+  {
+    const int64_t end = min(bend, bbegin + chunk_pairs);
+    const int64_t wbase = bbegin + wave * (kWave * R);
 #pragma unroll
-  for (int s = 0; s < R; ++s) {
-    const int i = wbase + s * kWave + lane;
-    e[s] = (i < end) ? ids[i] : 0;
+    for (int s = 0; s < R; ++s) {
+      const int64_t i = wbase + s * kWave + lane;
+      e[s] = (i < end) ? ids[i] : 0;
+    }
   }
 
   for (int j = tid; j < kLayoutWaves * kMaxExperts; j += kLayoutThreads) {
     (&mask[0][0])[j] = 0ull;
     (&wave_run[0][0])[j] = 0;
   }
+  for (int j = tid; j < kMaxExperts; j += kLayoutThreads) blk_run[j] = 0;
   if (tid == 0) flags_lds = 0;
   if (mapped) {
     for (int j = tid; j <= n_ids; j += kLayoutThreads) rep_off[j] = map.offsets[j];
     for (int j = tid; j < E; j += kLayoutThreads) rep_thr[j] = map.thresholds[j];
   }
-  int fl = duplicate_flags(ids, k, n_ids, begin, end);
+  int fl = duplicate_flags(ids, k, n_ids, bbegin, bend);
   __syncthreads();
-
-  if (mapped) {
-#pragma unroll
-    for (int s = 0; s < R; ++s) {
-      const int i = wbase + s * kWave + lane;
-      if (i >= end) continue;
-      int r = -1;
-      if (e[s] >= 0 && e[s] < n_ids) {
-        const uint32_t u = (uint32_t)(splitmix64(map.seed, (uint64_t)i) >> 32);
-        const int lo = rep_off[e[s]], hi = rep_off[e[s] + 1];
-        for (int c = lo; c < hi; ++c)
-          if (c >= 0 && c < E && u <= rep_thr[c]) {
-            r = c;
-            break;
-          }
-        if (r < 0) fl |= MOE_FLAG_REPLICA;
-      } else {
-        fl |= MOE_FLAG_ID_RANGE;
-      }
-      map.out[i] = r;
-      e[s] = r;  // ranked as a physical replica; -1 drops the pair
-    }
-  }
 
   const unsigned long long below_me = (1ull << lane) - 1ull;
-  int lr[R];
+  for (int c = 0; c < chunks; ++c) {
+    const int64_t begin = bbegin + (int64_t)c * chunk_pairs;
+    if (begin >= bend) break;  // workgroup-uniform
+    const int64_t end = min(bend, begin + chunk_pairs);
+    const int64_t wbase = begin + wave * (kWave * R);
+    if (c > 0) {
 #pragma unroll
-  for (int s = 0; s < R; ++s) {
-    const int i = wbase + s * kWave + lane;
-    const bool in = i < end;
-    const bool ok = in && e[s] >= 0 && e[s] < E;
-    if (in && !ok && !mapped) fl |= MOE_FLAG_ID_RANGE;
-    if (ok) atomicOr(&mask[wave][e[s]], 1ull << lane);
-    __builtin_amdgcn_wave_barrier();
-    unsigned long long m = 0;
-    int before = 0;
-    if (ok) {
-      m = mask[wave][e[s]];
-      before = wave_run[wave][e[s]];
+      for (int s = 0; s < R; ++s) {
+        const int64_t i = wbase + s * kWave + lane;
+        e[s] = (i < end) ? ids[i] : 0;
+      }
     }
-    __builtin_amdgcn_wave_barrier();
-    const int below = __popcll(m & below_me);
-    lr[s] = ok ? before + below : -1;
-    if (ok && below == 0) {
-      wave_run[wave][e[s]] = before + __popcll(m);
-      mask[wave][e[s]] = 0ull;
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-  __syncthreads();
 
-  // Exclusive prefix over waves, per expert; tot = this workgroup's count.
-  int tot = 0;
-  if (tid < E) {
+    if (mapped) {
 #pragma unroll
-    for (int w = 0; w < kLayoutWaves; ++w) {
-      const int c = wave_run[w][tid];
-      wave_run[w][tid] = tot;
-      tot += c;
+      for (int s = 0; s < R; ++s) {
+        const int64_t i = wbase + s * kWave + lane;
+        if (i >= end) continue;
+        int r = -1;
+        if (e[s] >= 0 && e[s] < n_ids) {
+          const uint32_t u = (uint32_t)(splitmix64(map.seed, (uint64_t)i) >> 32);
+          const int lo = rep_off[e[s]], hi = rep_off[e[s] + 1];
+          for (int q = lo; q < hi; ++q)
+            if (q >= 0 && q < E && u <= rep_thr[q]) {
+              r = q;
+              break;
+            }
+          if (r < 0) fl |= MOE_FLAG_REPLICA;
+        } else {
+          fl |= MOE_FLAG_ID_RANGE;
+        }
+        map.out[i] = r;
+        e[s] = r;  // ranked as a physical replica; -1 drops the pair
+      }
     }
+
+    int lr[R];
+#pragma unroll
+    for (int s = 0; s < R; ++s) {
+      const int64_t i = wbase + s * kWave + lane;
+      const bool in = i < end;
+      const bool ok = in && e[s] >= 0 && e[s] < E;
+      if (in && !ok && !mapped) fl |= MOE_FLAG_ID_RANGE;
+      if (ok) atomicOr(&mask[wave][e[s]], 1ull << lane);
+      __builtin_amdgcn_wave_barrier();
+      unsigned long long m = 0;
+      int before = 0;
+      if (ok) {
+        m = mask[wave][e[s]];
+        before = wave_run[wave][e[s]];
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int below = __popcll(m & below_me);
+      lr[s] = ok ? before + below : -1;
+      if (ok && below == 0) {
+        wave_run[wave][e[s]] = before + __popcll(m);
+        mask[wave][e[s]] = 0ull;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+
+    // Exclusive prefix over waves, per expert, after the earlier chunks.
+    int run = 0;
+    if (tid < E) {
+      run = blk_run[tid];
+#pragma unroll
+      for (int w = 0; w < kLayoutWaves; ++w) {
+        const int cnt = wave_run[w][tid];
+        wave_run[w][tid] = run;
+        run += cnt;
+      }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int s = 0; s < R; ++s) {
+      const int64_t i = wbase + s * kWave + lane;
+      if (i < end) ranks_out[i] = lr[s] >= 0 ? lr[s] + wave_run[wave][e[s]] : -1;
+    }
+    __syncthreads();
+    if (tid < E) {
+      blk_run[tid] = run;
+#pragma unroll
+      for (int w = 0; w < kLayoutWaves; ++w) wave_run[w][tid] = 0;
+    }
+    __syncthreads();
   }
   if (fl) atomicOr(&flags_lds, fl);
   __syncthreads();
+  const int tot = tid < E ? blk_run[tid] : 0;
 
-#pragma unroll
-  for (int s = 0; s < R; ++s) {
-    const int i = wbase + s * kWave + lane;
-    if (i < end) expand_idx[i] = lr[s] >= 0 ? lr[s] + wave_run[wave][e[s]] : -1;
-  }
-
-  if (block_hist == nullptr) {
+  if (ws.hist == nullptr) {
     // The whole batch was this workgroup: finish the layout here.
     write_counts_and_offsets(tot, E, align, wave_tot, counts, send, ranks);
     if (tid == 0 && status) *status = flags_lds;
-  } else {
-    if (tid < E) block_hist[blockIdx.x * E + tid] = tot;
-    if (tid == 0) block_flags[blockIdx.x] = flags_lds;
+    return;
   }
+  if (tid < E) ws.hist[(int64_t)blockIdx.x * E + tid] = tot;
+  if (tid == 0) ws.flags[blockIdx.x] = flags_lds;
+  // Count in with a device-scope release: after the workgroup barrier, one
+  // wave's release (an L2 write-back on this multi-XCD device) publishes
+  // every wave's writes before the increment.
+  __syncthreads();
+  if (tid == 0) {
+    const int before = __hip_atomic_fetch_add(ws.arrivals, 1, __ATOMIC_RELEASE,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    last_lds = (before == rank_blocks - 1) ? 1 : 0;
+    if (last_lds) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other histograms
+      flags_lds = 0;
+    }
+  }
+  __syncthreads();
+  if (!last_lds) return;
+  finish_layout(ws, rank_blocks, E, align, &wave_run[0][0], wave_tot, &flags_lds, counts, send,
+                status, ranks);
 }
 
+// Adds each workgroup's column prefix (from the arrival-ordered scan) to the
+// ranks within that workgroup.  One workgroup per ranking workgroup.
+// Workgroups past nblocks read token rows ahead instead.
 __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
-    const int32_t* __restrict__ ids, int32_t n_pairs, int32_t E, int32_t align,
-    int32_t pairs_per_block, int32_t nblocks, const int32_t* __restrict__ block_hist,
-    const int32_t* __restrict__ block_flags, int32_t* __restrict__ expand_idx,
-    int32_t* __restrict__ counts, int32_t* __restrict__ send, int32_t* __restrict__ status,
-    RankSplit ranks, ReadAhead ahead, int32_t ahead_blocks) {
-  if ((int32_t)blockIdx.x >= nblocks) {  // read-ahead workgroup: vectors [split, vecs)
+    const int32_t* __restrict__ ids, int32_t n_pairs, int32_t E, int64_t pairs_per_block,
+    const int32_t* __restrict__ base, int32_t* __restrict__ expand_idx, int32_t nblocks,
+    ReadAhead ahead, int32_t ahead_blocks) {
+  if ((int32_t)blockIdx.x >= nblocks) {
     read_ahead(ahead, nblocks, ahead_blocks, ahead.split, ahead.vecs);
     return;
   }
-  __shared__ int base[kMaxExperts];
-  __shared__ int wave_tot[kLayoutWaves];
-  const int b = blockIdx.x;
+  __shared__ int base_lds[kMaxExperts];
+  constexpr int kUnroll = 4;
   const int tid = threadIdx.x;
-  const bool last = (b == nblocks - 1);
-
-  __shared__ int flags_lds;
-  if (tid == 0) flags_lds = 0;
-  // This workgroup's pairs (the same split as the ranking pass): their loads
-  // do not depend on the histograms, so they are issued first and are in
-  // flight while the column sums below are formed.
-  const int begin = b * pairs_per_block;
-  const int end = min(n_pairs, begin + pairs_per_block);
-  int r[kLayoutMultiRounds], e[kLayoutMultiRounds];
+  const int64_t begin = (int64_t)blockIdx.x * pairs_per_block;
+  const int64_t end = min((int64_t)n_pairs, begin + pairs_per_block);
+  bool staged = false;
+  for (int64_t i0 = begin; i0 < end; i0 += kUnroll * kLayoutThreads) {
+    int r[kUnroll], e[kUnroll];
 #pragma unroll
-  for (int s = 0; s < kLayoutMultiRounds; ++s) {
-    const int i = begin + s * kLayoutThreads + tid;
-    r[s] = (i < end) ? expand_idx[i] : -1;
-    e[s] = (i < end) ? ids[i] : 0;
-  }
-  const int mine = (last && tid < E) ? block_hist[b * E + tid] : 0;
-  // Column sums over the earlier workgroups' histograms.  When E leaves
-  // threads over, `groups` threads share a column (E rounded up to a power
-  // of two, at most 16 per column), each summing every groups-th row, so one
-  // thread's chain of load batches is groups times shorter; the partial
-  // sums meet in LDS.
-  __shared__ int part[kLayoutThreads];
-  int epad = 1;
-  while (epad < E) epad <<= 1;
-  const int groups = min(16, kLayoutThreads / epad);  // workgroup-uniform
-  int own = 0;
-  if (groups == 1) {  // one thread per column: sum directly
-    if (tid < E) {
-      int sum = 0;
-#pragma unroll 8
-      for (int bb = 0; bb < b; ++bb) sum += block_hist[bb * E + tid];
-      base[tid] = sum;
-      own = sum + mine;
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = i0 + u * kLayoutThreads + tid;
+      r[u] = (i < end) ? expand_idx[i] : -1;
+      e[u] = (i < end) ? ids[i] : 0;
     }
-  } else {
-    const int col = tid & (epad - 1);
-    const int grp = tid / epad;
-    int sum = 0;
-    if (col < E && grp < groups) {
-#pragma unroll 8
-      for (int bb = grp; bb < b; bb += groups) sum += block_hist[bb * E + col];
+    if (!staged) {  // workgroup-uniform; overlaps the first loads
+      for (int j = tid; j < E; j += kLayoutThreads) base_lds[j] = base[blockIdx.x * E + j];
+      __syncthreads();
+      staged = true;
     }
-    part[tid] = sum;
-    __syncthreads();
-    if (tid < E) {
-      int total = 0;
-      for (int g = 0; g < groups; ++g) total += part[g * epad + tid];
-      base[tid] = total;
-      own = total + mine;
-    }
-  }
-  if (last) {  // workgroup-uniform
-    write_counts_and_offsets(own, E, align, wave_tot, counts, send, ranks);
-    int f = 0;
-    for (int bb = tid; bb < nblocks; bb += kLayoutThreads) f |= block_flags[bb];
-    if (f) atomicOr(&flags_lds, f);
-    __syncthreads();
-    if (tid == 0 && status) *status = flags_lds;
-  }
-  __syncthreads();
-
 #pragma unroll
-  for (int s = 0; s < kLayoutMultiRounds; ++s) {
-    const int i = begin + s * kLayoutThreads + tid;
-    if (r[s] >= 0) expand_idx[i] = r[s] + base[e[s]];
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = i0 + u * kLayoutThreads + tid;
+      if (r[u] >= 0) expand_idx[i] = r[u] + base_lds[e[u]];
+    }
   }
 }
 
@@ -330,32 +410,57 @@ LayoutPlan plan_layout(int32_t bs, int32_t k) {
     int r = 1;
     while ((int64_t)r * kLayoutThreads < p.n_pairs) r *= 2;
     p.rounds = r;
+    p.chunk_pairs = (int32_t)p.n_pairs;
+    p.chunks = 1;
   } else {
+    // Chunks of whole tokens, so that every token lies in one workgroup.
     p.rounds = kLayoutMultiRounds;
-    const int64_t ppb = (int64_t)kLayoutMultiRounds * kLayoutThreads;
+    p.chunk_pairs = (kLayoutThreads * kLayoutMultiRounds / k) * k;
+    const int64_t total_chunks = (p.n_pairs + p.chunk_pairs - 1) / p.chunk_pairs;
+    p.chunks = (int32_t)((total_chunks + kLayoutMaxBlocks - 1) / kLayoutMaxBlocks);
+    const int64_t ppb = (int64_t)p.chunks * p.chunk_pairs;
     p.blocks = (int32_t)((p.n_pairs + ppb - 1) / ppb);
   }
-  p.pairs_per_block = (int64_t)p.rounds * kLayoutThreads;
+  p.pairs_per_block = (int64_t)p.chunks * p.chunk_pairs;
   return p;
 }
 
+namespace {
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
 size_t layout_workspace_bytes(const LayoutPlan& p, int32_t num_experts) {
   if (p.blocks <= 1) return 0;
-  const size_t hist = (size_t)p.blocks * num_experts * sizeof(int32_t);
-  const size_t hist_aligned = (hist + 255) & ~(size_t)255;
-  return hist_aligned + (size_t)p.blocks * sizeof(int32_t);
+  return align256((size_t)p.blocks * num_experts * sizeof(int32_t)) +
+         align256((size_t)p.blocks * sizeof(int32_t)) + 256 +
+         align256((size_t)p.n_pairs * sizeof(int32_t));
+}
+
+LayoutScratch layout_scratch(const LayoutPlan& p, int32_t num_experts, void* workspace) {
+  LayoutScratch ws;
+  if (p.blocks <= 1) return ws;
+  char* base = static_cast<char*>(workspace);
+  const size_t hist = align256((size_t)p.blocks * num_experts * sizeof(int32_t));
+  const size_t flags = align256((size_t)p.blocks * sizeof(int32_t));
+  ws.hist = reinterpret_cast<int32_t*>(base);
+  ws.flags = reinterpret_cast<int32_t*>(base + hist);
+  ws.arrivals = reinterpret_cast<int32_t*>(base + hist + flags);
+  ws.ranks = reinterpret_cast<int32_t*>(base + hist + flags + 256);
+  return ws;
 }
 
 namespace {
 
 template <int R>
 void launch_rank(const LayoutPlan& plan, const int32_t* ids, int32_t k, int32_t E, int32_t align,
-                 int32_t* expand_idx, int32_t* hist, int32_t* bflags, int32_t* counts,
-                 int32_t* send, int32_t* status, const ReplicaMap& map, const RankSplit& ranks,
+                 int32_t* ranks_out, const LayoutScratch& ws, int32_t* counts, int32_t* send,
+                 int32_t* status, const ReplicaMap& map, const RankSplit& ranks,
                  hipStream_t stream, const ReadAhead& ahead, int32_t ahead_blocks) {
   launch_kernel(layout_rank_kernel<R>, plan.blocks + ahead_blocks, kLayoutThreads, stream,
-      ids, (int32_t)plan.n_pairs, k, E, align, expand_idx, hist, bflags, counts, send, status,
-      map, ranks, ahead, plan.blocks, ahead_blocks);
+      ids, (int32_t)plan.n_pairs, k, E, align, plan.chunk_pairs, plan.chunks, ranks_out, ws,
+      counts, send, status, map, ranks, ahead, plan.blocks, ahead_blocks);
 }
 
 }  // namespace
@@ -364,36 +469,33 @@ hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int
                          const LayoutPlan& plan, int32_t* counts, int32_t* send,
                          int32_t* expand_idx, int32_t* status, void* workspace,
                          const ReplicaMap& map, const RankSplit& ranks, hipStream_t stream,
-                         const ReadAhead& ahead) {
+                         const ReadAhead& ahead, bool defer_ranks) {
   const int32_t ahead_blocks =
       read_ahead_runs(plan, ahead) ? kReadAheadMaxBlocks - plan.blocks : 0;
-  int32_t* hist = nullptr;
-  int32_t* bflags = nullptr;
-  if (plan.blocks > 1) {
-    hist = static_cast<int32_t*>(workspace);
-    const size_t hist_bytes = ((size_t)plan.blocks * num_experts * sizeof(int32_t) + 255) &
-                              ~(size_t)255;
-    bflags = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + hist_bytes);
-  }
+  const bool finalize = plan.blocks > 1 && !defer_ranks;
+  // Without a finalize launch the ranking launch reads every row ahead.
+  ReadAhead ahead_used = ahead;
+  if (!finalize || ahead_blocks == 0) ahead_used.split = ahead.vecs;
+  const LayoutScratch ws = layout_scratch(plan, num_experts, workspace);
+  // With several workgroups and a scatter to follow, the ranks within the
+  // workgroups stay in the workspace and the scatter completes expand_idx.
+  int32_t* ranks_out = (plan.blocks > 1 && defer_ranks) ? ws.ranks : expand_idx;
   switch (plan.rounds) {
-    case 1: launch_rank<1>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, map, ranks, stream, ahead, ahead_blocks); break;
-    case 2: launch_rank<2>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, map, ranks, stream, ahead, ahead_blocks); break;
-    case 4: launch_rank<4>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, map, ranks, stream, ahead, ahead_blocks); break;
-    case 8: launch_rank<8>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                           send, status, map, ranks, stream, ahead, ahead_blocks); break;
-    default: launch_rank<16>(plan, ids, k, num_experts, align, expand_idx, hist, bflags, counts,
-                             send, status, map, ranks, stream, ahead, ahead_blocks); break;
+    case 1: launch_rank<1>(plan, ids, k, num_experts, align, ranks_out, ws, counts, send,
+                           status, map, ranks, stream, ahead_used, ahead_blocks); break;
+    case 2: launch_rank<2>(plan, ids, k, num_experts, align, ranks_out, ws, counts, send,
+                           status, map, ranks, stream, ahead_used, ahead_blocks); break;
+    default: launch_rank<4>(plan, ids, k, num_experts, align, ranks_out, ws, counts, send,
+                            status, map, ranks, stream, ahead_used, ahead_blocks); break;
   }
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || plan.blocks <= 1) return err;
+  if (err != hipSuccess || plan.blocks <= 1 || defer_ranks) return err;
   // The finalize pass looks pairs up by the id they were ranked under.
   const int32_t* ranked_ids = map.offsets != nullptr ? map.out : ids;
-  launch_kernel(layout_finalize_kernel, plan.blocks + ahead_blocks, kLayoutThreads, stream,
-      ranked_ids, (int32_t)plan.n_pairs, num_experts, align, (int32_t)plan.pairs_per_block,
-      plan.blocks, hist, bflags, expand_idx, counts, send, status, ranks, ahead, ahead_blocks);
+  const int32_t finalize_ahead = ahead_used.split < ahead_used.vecs ? ahead_blocks : 0;
+  launch_kernel(layout_finalize_kernel, plan.blocks + finalize_ahead, kLayoutThreads, stream,
+      ranked_ids, (int32_t)plan.n_pairs, num_experts, plan.pairs_per_block,
+      (const int32_t*)ws.hist, expand_idx, plan.blocks, ahead_used, finalize_ahead);
   return hipGetLastError();
 }
 

@@ -102,16 +102,19 @@ __device__ __forceinline__ void fetch_pair_meta(PairMeta& m, int32_t t, int32_t 
 
 // Turns fetched metadata into workgroup-uniform routes: destination row
 // slot[j] (-1 = pair skipped) and weight w[j], using the send counts staged
-// in LDS.  A slot outside [0, cap) is skipped and, when `report` is set,
-// flagged through `status`.
+// in LDS (plus, when `base_lds` is given, the column prefix of the ranking
+// workgroup that ranked the token, for ranks left within that workgroup).
+// A slot outside [0, cap) is skipped and, when `report` is set, flagged
+// through `status`.
 template <int KMAX>
-__device__ __forceinline__ void resolve_routes(const PairMeta& m, const int* send_lds, int32_t k,
-                                               int32_t E, int64_t cap, int64_t (&slot)[KMAX],
+__device__ __forceinline__ void resolve_routes(const PairMeta& m, const int* send_lds,
+                                               const int* base_lds, int32_t k, int32_t E,
+                                               int64_t cap, int64_t (&slot)[KMAX],
                                                float (&w)[KMAX], int32_t* status, bool report) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t my_slot = -1;
   if (lane < k && m.e >= 0 && m.e < E && m.r >= 0) {
-    const int64_t s = (int64_t)send_lds[m.e] + m.r;
+    const int64_t s = (int64_t)send_lds[m.e] + (base_lds ? base_lds[m.e] : 0) + m.r;
     if (s >= 0 && s < cap)
       my_slot = s;
     else if (report && status)
@@ -169,20 +172,60 @@ __device__ __forceinline__ u32x4 quantize16_e4m3(const u32x4& a, const u32x4& b,
   return codes;
 }
 
-// Copies ep_send_counts[0..E] into LDS (one pass per workgroup).
-__device__ __forceinline__ void stage_send(int* send_lds, const int32_t* __restrict__ send,
-                                           int32_t E) {
+// Copies n ints (1 <= n <= N) from global memory into LDS with a
+// THREADS-wide workgroup in two steps, so that a caller can put other loads
+// between them: load() issues every load into registers, store() writes them
+// to LDS (the caller synchronises).  Staging then costs one memory round
+// trip.  Neither step branches (a lane past the end repeats element n - 1
+// and stores it past the end, into the kSlots-int LDS area), so a wait for
+// these loads need not cover loads the caller issues after them.
+template <int THREADS, int N>
+struct StagedInts {
+  static constexpr int kPer = (N + THREADS - 1) / THREADS;
+  static constexpr int kSlots = kPer * THREADS;  // LDS ints store() writes
+  int v[kPer];
+  __device__ __forceinline__ void load(const int32_t* __restrict__ src, int32_t n) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = i * THREADS + (int)threadIdx.x;
+      v[i] = src[e < n ? e : n - 1];
+    }
+  }
+  __device__ __forceinline__ void store(int* lds) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) lds[i * THREADS + (int)threadIdx.x] = v[i];
+  }
+};
+
+// Keeps the compiler from moving memory accesses across this point (no
+// instruction is emitted): loads issued before it stay before it, in order.
+__device__ __forceinline__ void keep_order() { __asm__ volatile("" ::: "memory"); }
+
+// ep_send_counts[0..E] (E + 1 ints) staged by a THREADS-wide workgroup.
+template <int THREADS>
+using StagedSend = StagedInts<THREADS, kMaxExperts + 1>;
+
+// Copies ep_send_counts[0..E] into LDS with a workgroup of any size (one
+// load per thread and round when blockDim.x >= E + 1).
+__device__ __forceinline__ void stage_send_any(int* send_lds, const int32_t* __restrict__ send,
+                                               int32_t E) {
   for (int e = threadIdx.x; e <= E; e += blockDim.x) send_lds[e] = send[e];
   __syncthreads();
 }
 
+// Zeros read in place of a row that is absent (no shared row), so that the
+// load needs no branch.
+__device__ const u32x4 kZeroVec = {0u, 0u, 0u, 0u};
+
 // ---- layout ---------------------------------------------------------------
-// Pairs ranked per workgroup and round trip parameters, chosen on the host.
+// Ranking workgroups and their work, chosen on the host.
 struct LayoutPlan {
   int64_t n_pairs;          // bs * k
-  int32_t blocks;           // workgroups of the ranking pass
-  int32_t rounds;           // rounds of kLayoutThreads pairs per workgroup
-  int64_t pairs_per_block;  // rounds * kLayoutThreads
+  int32_t blocks;           // workgroups of the ranking pass (<= kLayoutMaxBlocks)
+  int32_t rounds;           // rounds of kLayoutThreads pairs per chunk
+  int32_t chunk_pairs;      // pairs per chunk: whole tokens, at most rounds * kLayoutThreads
+  int32_t chunks;           // chunks per ranking workgroup
+  int64_t pairs_per_block;  // chunks * chunk_pairs
 };
 constexpr int kLayoutWaves = 8;
 constexpr int kLayoutThreads = kLayoutWaves * kWave;   // 512 pairs per round
@@ -193,9 +236,31 @@ constexpr int kLayoutThreads = kLayoutWaves * kWave;   // 512 pairs per round
 #define MOE_LAYOUT_MULTI_ROUNDS 4
 #endif
 // One workgroup ranks up to kLayoutThreads * kLayoutSingleMaxRounds pairs by
-// itself; larger batches use workgroups of kLayoutMultiRounds rounds each.
+// itself; larger batches use workgroups of chunks of kLayoutMultiRounds
+// rounds each, at most kLayoutMaxBlocks workgroups (more chunks per
+// workgroup beyond that), so the last workgroup's scan over the workgroups'
+// histograms stays bounded.
 constexpr int kLayoutSingleMaxRounds = MOE_LAYOUT_SINGLE_ROUNDS;
 constexpr int kLayoutMultiRounds = MOE_LAYOUT_MULTI_ROUNDS;
+constexpr int kLayoutMaxBlocks = 256;
+
+// The multi-workgroup layout's device workspace.  `arrivals` must be zero
+// when a call starts; every call leaves it zero again.
+struct LayoutScratch {
+  int32_t* hist = nullptr;      // [blocks][E] histograms, then their column prefix
+  int32_t* flags = nullptr;     // [blocks] status bits per workgroup
+  int32_t* arrivals = nullptr;  // workgroups that have published their histogram
+  int32_t* ranks = nullptr;     // [n_pairs] ranks within the workgroup (deferred ranks)
+};
+
+// Ranks that a multi-workgroup layout left within their ranking workgroup
+// (moe_dispatch_fused): the scatter adds the workgroup's column prefix and
+// writes the final expand_idx.  base == nullptr: ranks are final.
+struct DeferredRanks {
+  const int32_t* base = nullptr;  // LayoutScratch::hist after the scan
+  int32_t tokens_per_block = 0;   // tokens per ranking workgroup
+  int32_t* expand_idx = nullptr;  // final ranks, written by each token's first chunk
+};
 
 // Optional logical-expert -> physical-replica choice fused into the ranking
 // pass (offsets == nullptr: ids are ranked as given).
@@ -215,21 +280,29 @@ struct RankSplit {
   int32_t ranks = 0;
 };
 
-// Token rows that the layout launches read ahead.  The layout is latency
-// bound and leaves HBM nearly idle, so up to kReadAheadMaxBlocks workgroups
-// of each of its two launches (together with the ranking workgroups) read
-// the rows the scatter will need with ordinary loads, which allocate in the
-// 256 MB Infinity Cache; the scatter then finds them there instead of
-// mixing row reads from HBM into its write stream.  At most
-// kReadAheadMaxBytes are read ahead (half the cache).
+// Token rows that the layout's ranking launch reads ahead.  The layout is
+// latency bound and leaves HBM nearly idle, so up to kReadAheadMaxBlocks
+// workgroups (together with the ranking workgroups) read the rows the
+// scatter will need with ordinary loads, which allocate in the 256 MB
+// Infinity Cache; the scatter then finds them there instead of mixing row
+// reads from HBM into its write stream.  At most kReadAheadMaxBytes are read
+// ahead (half the cache).
 struct ReadAhead {
   const u32x4* base = nullptr;
   int64_t vecs = 0;   // 16-byte vectors, from base
-  int64_t split = 0;  // the rank launch reads [0, split), the finalize launch [split, vecs)
+  int64_t split = 0;  // with a finalize launch: the ranking launch reads [0, split)
 };
-#ifndef MOE_READ_AHEAD_RANK_PERCENT
-#define MOE_READ_AHEAD_RANK_PERCENT 50
+// Whether moe_dispatch_fused leaves the ranks within the ranking workgroups
+// to the scatter (two launches) or completes them in a finalize launch first
+// (three launches, the read-ahead split between the ranking and finalize
+// launches at MOE_READ_AHEAD_RANK_PERCENT).
+#ifndef MOE_FUSED_DEFER
+#define MOE_FUSED_DEFER 1
 #endif
+#ifndef MOE_READ_AHEAD_RANK_PERCENT
+#define MOE_READ_AHEAD_RANK_PERCENT 60
+#endif
+constexpr bool kFusedDefer = MOE_FUSED_DEFER != 0;
 constexpr int kReadAheadRankPercent = MOE_READ_AHEAD_RANK_PERCENT;
 constexpr int kReadAheadMaxBlocks = 240;  // of the 256 compute units, with the ranking workgroups
 constexpr int64_t kReadAheadMaxBytes = int64_t(128) << 20;
@@ -279,18 +352,22 @@ inline void launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, hipS
 
 LayoutPlan plan_layout(int32_t bs, int32_t k);
 
-// Read-ahead workgroups only ride along the two-launch layout, and only
+// Read-ahead workgroups only ride along a multi-workgroup layout, and only
 // while the ranking workgroups leave compute units free.
 inline bool read_ahead_runs(const LayoutPlan& plan, const ReadAhead& ahead) {
   return plan.blocks > 1 && ahead.vecs > 0 && plan.blocks < kReadAheadMaxBlocks;
 }
 size_t layout_workspace_bytes(const LayoutPlan& p, int32_t num_experts);
+LayoutScratch layout_scratch(const LayoutPlan& p, int32_t num_experts, void* workspace);
 
+// The layout launch(es).  With defer_ranks and several ranking workgroups,
+// only the ranking launch runs: expand_idx is left for a scatter launched
+// with the matching DeferredRanks.
 hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int32_t align,
                          const LayoutPlan& plan, int32_t* counts, int32_t* send,
                          int32_t* expand_idx, int32_t* status, void* workspace,
                          const ReplicaMap& map, const RankSplit& ranks, hipStream_t stream,
-                         const ReadAhead& ahead = ReadAhead{});
+                         const ReadAhead& ahead = ReadAhead{}, bool defer_ranks = false);
 
 // Batches of at most this many pairs fit one layout workgroup; the fused
 // layout + bf16 scatter derives the layout in every scatter workgroup.
@@ -312,17 +389,21 @@ hipError_t launch_dispatch_fused_bf16(const void* x, int64_t x_stride, int32_t b
                                       int64_t capacity_rows, hipStream_t stream);
 
 // ---- dispatch / combine -----------------------------------------------------
+// `expand_idx` holds final ranks, or with deferred.base the ranks within
+// the ranking workgroups (then the kernels write deferred.expand_idx).
 hipError_t launch_dispatch_bf16(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
                                 const int32_t* ids, const int32_t* expand_idx,
                                 const int32_t* send, int32_t k, int32_t num_experts,
                                 void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
-                                int32_t* status, hipStream_t stream, bool rows_cached = false);
+                                int32_t* status, hipStream_t stream, bool rows_cached = false,
+                                const DeferredRanks& deferred = DeferredRanks{});
 
 hipError_t launch_dispatch_fp8(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
                                const int32_t* ids, const int32_t* expand_idx,
                                const int32_t* send, int32_t k, int32_t num_experts,
                                void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
-                               float* quant_scales, int32_t* status, hipStream_t stream);
+                               float* quant_scales, int32_t* status, hipStream_t stream,
+                               const DeferredRanks& deferred = DeferredRanks{});
 
 hipError_t launch_combine(const void* y, int64_t y_stride, int64_t capacity_rows,
                           const int32_t* ids, const int32_t* expand_idx, const int32_t* send,

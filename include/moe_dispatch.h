@@ -68,7 +68,8 @@ enum moe_flag {
     MOE_FLAG_REPLICA = 8       /* a replica table gave an expert no replica for some draw */
 };
 
-/* Version of this interface (incremented on any signature change). */
+/* Version of this interface (incremented on any change of a signature or of
+ * a caller's obligations; 2: the layout workspace must start zero-filled). */
 int moe_abi_version(void);
 
 /* Human-readable text of a moe_status value (static storage). */
@@ -86,9 +87,16 @@ const char* moe_status_string(int status);
  */
 int64_t moe_dispatch_capacity(int32_t bs, int32_t k, int32_t num_experts, int32_t align);
 
-/* Bytes of device workspace moe_dispatch_layout needs for this shape (0 when
- * the whole layout fits one workgroup; then `workspace` may be NULL).
- * Returns 0 for invalid arguments as well; the layout call reports those. */
+/* Bytes of device workspace moe_dispatch_layout (and the fused and
+ * replica-aware calls) need for this shape: 0 when the whole layout fits one
+ * workgroup (bs*k <= 2048; then `workspace` may be NULL).  Returns 0 for
+ * invalid arguments as well; the layout call reports those.
+ * The workspace must be zero-filled before its first use (for example with
+ * hipMemset, or a fill kernel where a memset node is unwanted, as under
+ * graph capture); every call returns it to that state when its kernels
+ * finish.  It holds the ranking workgroups' histograms, which the last
+ * workgroup to finish scans, and the arrival counter that tells a workgroup
+ * it is the last. */
 size_t moe_dispatch_layout_workspace_size(int32_t bs, int32_t k, int32_t num_experts);
 
 /*
@@ -119,10 +127,19 @@ size_t moe_dispatch_layout_workspace_size(int32_t bs, int32_t k, int32_t num_exp
  *                     MOE_FLAG_DUP_ID, overwritten (not accumulated).
  *                     Out-of-range pairs are excluded from the counts;
  *                     repeated ids are laid out like distinct ones.
- *  workspace      in  device scratch of workspace_bytes >=
+ *  workspace      in/out device scratch of workspace_bytes >=
  *                     moe_dispatch_layout_workspace_size(bs, k, num_experts),
- *                     16-byte aligned; contents need no initialisation.
- * The result is deterministic (no atomics decide any position).
+ *                     16-byte aligned, zero-filled before its first use (see
+ *                     moe_dispatch_layout_workspace_size); calls that share a
+ *                     workspace must not overlap.
+ * The result is deterministic (no atomics decide any position).  Batches of
+ * more than 2048 pairs take two launches: ranking workgroups of whole tokens
+ * (at most 256, each walking chunks of at most 2048 pairs) write their
+ * ranks and per-expert histograms, and the last of them to finish turns the
+ * histograms into each expert's exclusive prefix over workgroups (a
+ * device-wide scan in which every histogram entry is read and written once)
+ * and writes the counts and ep_send_counts; a second launch adds each
+ * workgroup's prefix to its ranks.  Work grows linearly with bs*k.
  */
 int moe_dispatch_layout(const int32_t* expert_ids, int32_t bs, int32_t k, int32_t num_experts,
                         int32_t align, int32_t* expert_counts, int32_t* ep_send_counts,
@@ -235,15 +252,17 @@ int moe_dispatch(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
  * scatter workgroup derives the whole layout from the ids in on-chip memory,
  * so no separate layout launch or wait precedes the scatter (the TEMPO
  * summary, section 2, folds count gathering into the dispatch kernel; here
- * the counts, offsets and ranks are folded in).  Larger batches run the
- * layout and dispatch kernels in sequence; the layout launches, which are
- * latency bound, then also read the token rows x ahead (ordinary loads, at
- * most 128 MB, x contiguous) so that the scatter finds them in the 256 MB
- * Infinity Cache instead of interleaving row reads from HBM with its
- * writes.  HBM still reads x once.  When every row was read ahead, the bf16
- * scatter runs with fewer waves in flight (at most 8 workgroups of 64
- * threads per compute unit), which narrows the window of destination rows
- * being written at once.
+ * the counts, offsets and ranks are folded in).  Larger batches take two
+ * launches: the layout's ranking launch (its last workgroup scans the
+ * histograms, as in moe_dispatch_layout), then the scatter, which adds each
+ * token's workgroup prefix to the ranks and writes expand_idx itself, so no
+ * finalize launch sits between them.  The ranking launch, which is latency
+ * bound, also reads the token rows x ahead (ordinary loads, at most 128 MB,
+ * x contiguous) so that the scatter finds them in the 256 MB Infinity Cache
+ * instead of interleaving row reads from HBM with its writes.  When every
+ * row was read ahead, the bf16 scatter runs with fewer waves in flight (at
+ * most 8 workgroups of 64 threads per compute unit), which narrows the
+ * window of destination rows being written at once.
  *
  *  x, x_stride, bs, hidden                   as for moe_dispatch.
  *  expert_ids, k, num_experts, align         as for moe_dispatch_layout.
@@ -324,11 +343,12 @@ int moe_combine_fp8(const void* expand_x, int64_t expand_x_stride, int64_t capac
  * expert_ids = replica_ids and num_experts = num_replicas, on the same
  * stream, bit for bit (replica ids, counts, offsets, ranks, dispatched rows,
  * padding rows left unwritten, e4m3 codes and scales, status bits).  As in
- * moe_dispatch_fused, when the layout takes two launches (bs*k > 2048) they
- * also read the token rows ahead into the Infinity Cache (x contiguous, at
- * most 128 MB), and a bf16 scatter of rows that were all read ahead runs
- * with fewer waves in flight.  Batches of at most 2048 pairs take one layout
- * launch and the scatter launch.
+ * moe_dispatch_fused, batches of more than 2048 pairs take the ranking
+ * launch, which also reads the token rows ahead into the Infinity Cache (x
+ * contiguous, at most 128 MB), and the scatter, which completes expand_idx;
+ * a bf16 scatter of rows that were all read ahead runs with fewer waves in
+ * flight.  Batches of at most 2048 pairs take one layout launch and the
+ * scatter launch.
  *
  *  x, x_stride, hidden, expand_x, expand_x_stride, capacity_rows, out_dtype,
  *  quant_scales               as for moe_dispatch (over num_replicas).

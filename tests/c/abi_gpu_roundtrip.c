@@ -112,7 +112,10 @@ static int run_case(int32_t bs, int32_t hidden, int32_t e, int32_t k, int path) 
   CHECK_HIP(hipMalloc(&d_x, sizeof(uint16_t) * bs * hidden));
   CHECK_HIP(hipMalloc(&d_ex, sizeof(uint16_t) * cap * hidden));
   CHECK_HIP(hipMalloc(&d_out, sizeof(uint16_t) * bs * hidden));
-  if (ws_bytes > 0) CHECK_HIP(hipMalloc(&d_ws, ws_bytes));
+  if (ws_bytes > 0) {
+    CHECK_HIP(hipMalloc(&d_ws, ws_bytes));
+    CHECK_HIP(hipMemset(d_ws, 0, ws_bytes)); /* zero-filled before its first use */
+  }
   CHECK_HIP(hipMemcpy(d_ids, ids, sizeof(int32_t) * n, hipMemcpyHostToDevice));
   CHECK_HIP(hipMemcpy(d_scales, scales, sizeof(float) * n, hipMemcpyHostToDevice));
   CHECK_HIP(hipMemcpy(d_x, x, sizeof(uint16_t) * bs * hidden, hipMemcpyHostToDevice));
@@ -152,8 +155,9 @@ static int run_case(int32_t bs, int32_t hidden, int32_t e, int32_t k, int path) 
                         k, ranked, d_out, d_status, NULL));
   CHECK_HIP(hipDeviceSynchronize());
   if (path == 3) {
-    /* the fused call launches one kernel at this size or three above 2048
-       pairs, the combine one: every taken pair holds a positive kernel time */
+    /* the fused call launches one kernel at this size or two above 2048
+       pairs (ranking with its scan, then the scatter), the combine one:
+       every taken pair holds a positive kernel time */
     timed = 4 - moe_time_unused_launches();
     CHECK_MOE(moe_time_next_launches(NULL, NULL, 0));
     for (int i = 0; i < timed; ++i) {
@@ -179,7 +183,7 @@ static int run_case(int32_t bs, int32_t hidden, int32_t e, int32_t k, int path) 
   }
   if (total != n || status != 0) bad = 1;
   if (memcmp(out, x, sizeof(uint16_t) * bs * hidden) != 0) bad = 1;
-  if (path == 3 && timed != (n <= 2048 ? 2 : 4)) bad = 1;
+  if (path == 3 && timed != (n <= 2048 ? 2 : 3)) bad = 1;
   static const char* names[] = {"separate", "fused", "fused replicated", "fused, timed"};
   printf("case bs=%d H=%d E=%d K=%d %s: %s\n", bs, hidden, e, k, names[path],
          bad ? "MISMATCH" : "round trip exact");
@@ -198,11 +202,11 @@ int main(void) {
   bad |= run_case(37, 256, 16, 4, 0);    /* one layout workgroup */
   bad |= run_case(700, 512, 64, 8, 0);   /* workspace, two layout launches */
   bad |= run_case(128, 1024, 256, 8, 1); /* fused, one launch */
-  bad |= run_case(600, 512, 64, 8, 1);   /* fused, layout launches with read-ahead */
+  bad |= run_case(600, 512, 64, 8, 1);   /* fused, ranking launch with read-ahead */
   bad |= run_case(300, 256, 32, 4, 2);   /* replica-aware fused, 64 replicas, one layout launch */
   bad |= run_case(900, 512, 128, 8, 2);  /* replica-aware fused, 256 replicas, read-ahead */
   bad |= run_case(128, 1024, 256, 8, 3); /* timed: one fused launch + combine */
-  bad |= run_case(600, 512, 64, 8, 3);   /* timed: rank, finalize, scatter + combine */
+  bad |= run_case(600, 512, 64, 8, 3);   /* timed: ranking + scan, scatter + combine */
   if (!bad) printf("ok\n");
   return bad;
 }

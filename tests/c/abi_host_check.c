@@ -25,7 +25,7 @@ int main(void) {
   int64_t loads[2], before = 0, after = 0, ideal = 0;
   const int32_t expert_counts[4] = {1024, 0, 0, 0};
 
-  expect(moe_abi_version() == 1, "abi version");
+  expect(moe_abi_version() == 2, "abi version");
   expect(strcmp(moe_status_string(MOE_OK), "ok") == 0, "status string ok");
   expect(strstr(moe_status_string(99), "unknown") != NULL, "unknown status string");
 

@@ -68,7 +68,7 @@ def test_library_exports_only_the_c_abi():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     for code in range(5):
         assert lib.moe_status_string(code)
     assert b"unknown" in lib.moe_status_string(99)

@@ -69,8 +69,8 @@ def test_captured_step_replays_match_the_oracle(bs, hidden, e, k, with_shared, p
                      torch.empty(e + 1, dtype=torch.int32, device=dev),
                      torch.empty(bs * k, dtype=torch.int32, device=dev),
                      torch.empty(1, dtype=torch.int32, device=dev))
-    ws = torch.empty(max(moe.moe_dispatch_layout_workspace_size(bs, k, e), 16),
-                     dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(moe.moe_dispatch_layout_workspace_size(bs, k, e), 16),
+                     dtype=torch.uint8, device=dev)  # zero-filled before its first use
     expand_x = torch.empty((cap, hidden), dtype=torch.bfloat16, device=dev)
     out = torch.empty((bs, hidden), dtype=torch.bfloat16, device=dev)
 

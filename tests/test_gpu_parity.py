@@ -748,9 +748,57 @@ def test_maximum_row_two_launch_fused():
 
 
 def test_layout_many_workgroups_every_expert_count():
-    """Hundreds of ranking workgroups with E from 1 to 512, so the finalize
-    pass's column sums run with 16, 8, 4, 2 and 1 threads per column."""
+    """Tens to 256 ranking workgroups with E from 1 to 512, so the last
+    workgroup's column scan runs with 512 down to 1 threads per column."""
     rng = np.random.default_rng(103)
     for bs, e, k in [(200000, 1, 1), (60000, 3, 2), (100000, 8, 2), (30000, 100, 8),
                      (40000, 300, 4), (30000, 512, 16)]:
         assert_layout_equal(random_ids(rng, bs, e, k), e, 128)
+
+
+def rotated_ids(rng, bs, e, k):
+    """Distinct ids per row at sizes where a per-row argsort is too slow:
+    (h_t + j) mod E for a uniform start h_t (k <= E)."""
+    h = rng.integers(0, e, size=bs, dtype=np.int32)
+    ids = np.empty((bs, k), np.int32)
+    for j in range(k):
+        np.add(h, j, out=ids[:, j])
+        np.remainder(ids[:, j], e, out=ids[:, j])
+    return ids
+
+
+def test_layout_multi_chunk_workgroups():
+    """Batches beyond 256 workgroups of 2048 pairs: each ranking workgroup
+    walks several chunks of whole tokens (K not dividing 2048 as well), and
+    the scan over the workgroups' histograms runs once."""
+    rng = np.random.default_rng(104)
+    for bs, e, k in [(100000, 37, 7), (80000, 512, 16), (600000, 1, 1), (200001, 200, 3),
+                     (140000, 64, 5)]:
+        (c, s, r, f), _ = assert_layout_equal(rotated_ids(rng, bs, e, k), e, 128)
+        assert int(c.sum()) == bs * k and f == 0
+
+
+@pytest.mark.parametrize("pairs,e,k", [(4 << 20, 256, 8), (16 << 20, 512, 8)])
+def test_layout_millions_of_pairs(pairs, e, k):
+    """The work-efficient scan at 4M and 16M pairs, bit-exact."""
+    rng = np.random.default_rng(105 + pairs % 97)
+    ids = rotated_ids(rng, pairs // k, e, k)
+    ids[::1013] = np.arange(k, dtype=np.int32)[::-1]  # a recurring token on the same experts
+    (c, s, r, f), _ = assert_layout_equal(ids, e, 128)
+    assert int(c.sum()) == pairs and f == 0
+
+
+def test_layout_largest_batch():
+    """The largest batch the argument rules admit at E = 512, K = 16,
+    align = 128: 67,104,807 tokens (1,073,676,912 pairs), whose padded
+    capacity is exactly 2^30 rows.  Layout only (the ids need no token rows)."""
+    moe = moe_mod()
+    e, k, align = 512, 16, 128
+    bs = 67104807
+    assert moe.moe_dispatch_capacity(bs, k, e, align) == 1 << 30
+    with pytest.raises(moe.MoeError):
+        moe.moe_dispatch_capacity(bs + 1, k, e, align)
+    rng = np.random.default_rng(106)
+    ids = rotated_ids(rng, bs, e, k)
+    (c, s, r, f), _ = assert_layout_equal(ids, e, align)
+    assert int(c.sum()) == bs * k and f == 0

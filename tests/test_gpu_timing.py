@@ -25,10 +25,10 @@ def new_pairs(n):
     return pairs
 
 
-@pytest.mark.parametrize("bs,expect_launches", [(600, 4), (100, 2)])
+@pytest.mark.parametrize("bs,expect_launches", [(600, 3), (100, 2)])
 def test_bound_events_time_each_launch(bs, expect_launches):
-    """Two-launch layout + dispatch + combine (600 tokens, 4800 pairs) and the
-    single fused launch + combine (100 tokens, 800 pairs)."""
+    """Ranking launch (with its scan) + scatter + combine (600 tokens, 4800
+    pairs) and the single fused launch + combine (100 tokens, 800 pairs)."""
     import combine_moe_dispatch_layout_amd as moe
     h, e, k = 1024, 64, 8
     rng = np.random.default_rng(bs)
