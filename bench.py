@@ -458,7 +458,11 @@ def main():
         return {"layout": sum(ms[:-2]), "dispatch": ms[-2], "combine": ms[-1],
                 "layout_launches": len(ms) - 2}
 
-    for i in range(args.warmup):
+    # Warm-up: at least one step per buffer set, so that every set has run
+    # once before the timed region; the steps run are reported as
+    # warmup_steps_run.
+    warmup_run = max(args.warmup, sets)
+    for i in range(warmup_run):
         step(bufs[i % sets])
     torch.cuda.synchronize()
 
@@ -556,6 +560,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warmup_run,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

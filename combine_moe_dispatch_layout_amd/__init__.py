@@ -6,6 +6,14 @@ kernels; this module only marshals torch tensors (device memory and the
 current stream) into pointers.  If the library is not built the import of the
 entry points fails loudly -- there is no fallback.
 
+Before a call reaches the library, every tensor it passes is checked against
+the call's sizes (device, dtype, contiguity, rows and columns, lengths), so
+a mismatch raises ValueError instead of reaching the GPU.  The routing and
+scatter calls take ``check=True`` to wait for the GPU and raise
+MoeStatusError when the status word reports dropped pairs (a row beyond
+capacity_rows, an out-of-range id, a replica table without a replica) or
+repeated ids; it is off by default because it synchronises.
+
 Entry points (same names as the C ABI):
 
 * ``moe_dispatch_layout(expert_ids, num_experts, align=128)`` ->
@@ -14,7 +22,7 @@ Entry points (same names as the C ABI):
   ``expand_x`` (and ``quant_scales`` for e4m3)
 * ``moe_dispatch_fused(x, expert_ids, num_experts, align=128)`` ->
   ``(Layout, expand_x)`` (and ``quant_scales`` for e4m3): layout + dispatch in
-  one call, one kernel launch for batches of at most 2048 pairs
+  one call, one kernel launch for batches of at most 2048 pairs, two above
 * ``moe_combine(expand_x, expert_ids, expand_idx, ep_send_counts,
   expert_scales, shared_expert_x)`` -> ``x_out``
 * ``moe_combine_fp8(expand_x_codes, quant_scales, ...)`` -> ``x_out`` (expert
@@ -47,7 +55,7 @@ from typing import NamedTuple, Optional
 import torch
 
 __all__ = [
-    "MoeError", "Layout", "library_path", "load_library",
+    "MoeError", "MoeStatusError", "Layout", "library_path", "load_library",
     "moe_dispatch_capacity", "moe_dispatch_layout_workspace_size",
     "moe_dispatch_layout", "moe_dispatch_layout_ep", "moe_dispatch_layout_replicated",
     "moe_dispatch", "moe_dispatch_fused", "moe_dispatch_fused_replicated", "moe_combine",
@@ -129,10 +137,37 @@ def _check(rc: int) -> None:
         raise MoeError(rc, load_library().moe_status_string(rc).decode())
 
 
+class MoeStatusError(MoeError):
+    """Raised by calls made with ``check=True`` when the device-side status
+    word reports pairs that were dropped or malformed routing."""
+
+    def __init__(self, flags: int, call: str):
+        names = [n for bit, n in ((MOE_FLAG_ID_RANGE, "ID_RANGE"), (MOE_FLAG_DUP_ID, "DUP_ID"),
+                                  (MOE_FLAG_GUARD, "GUARD"), (MOE_FLAG_REPLICA, "REPLICA"))
+                 if flags & bit]
+        super().__init__(flags, f"{call}: status flags {'|'.join(names)}")
+        self.flags = flags
+
+
+def _raise_on_status(status: torch.Tensor, call: str) -> None:
+    """check=True: wait for the call (a host synchronisation) and raise on
+    any status bit: out-of-range ids, repeated ids in a row, a slot beyond
+    capacity_rows (its pair was dropped) or a replica table without a
+    replica for some draw."""
+    flags = int(status.reshape(-1)[0].item())
+    if flags:
+        raise MoeStatusError(flags, call)
+
+
 # The current stream's raw handle.  torch's raw getter skips building a
 # Stream object (about 0.1 us against 1.9 us per call, which matters for
 # decode-sized steps); the public API serves where it is absent.
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+# Device type every tensor argument must have.  The argument checks below
+# run before any library call; the CPU test tier sets this to "cpu" (with the
+# library stubbed out) to exercise them without a GPU.
+_DEVICE_TYPE = "cuda"
 
 
 def _stream(t: torch.Tensor) -> Optional[int]:
@@ -145,13 +180,30 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _need(t: torch.Tensor, dtype: torch.dtype, name: str, contiguous: bool = True) -> None:
-    if not t.is_cuda:
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _need(t, dtype, name: str, contiguous: bool = True, device=None) -> None:
+    """t is a tensor of `dtype` (a dtype or a tuple of them) on the library's
+    device type (and on `device` when given), contiguous unless told not."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if t.device.type != _DEVICE_TYPE:
         raise ValueError(f"{name} must be a device tensor")
-    if t.dtype != dtype:
-        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call's tensors on {device}")
+    dtypes = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(map(str, dtypes))}, got {t.dtype}")
     if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _need_len(t: torch.Tensor, n: int, name: str) -> None:
+    """A contiguous array the kernels index up to element n - 1."""
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {n}")
 
 
 def _row_stride(t: torch.Tensor, name: str) -> int:
@@ -160,11 +212,90 @@ def _row_stride(t: torch.Tensor, name: str) -> int:
     return t.stride(0)
 
 
+def _need_rows(t: torch.Tensor, rows: int, cols: int, name: str) -> int:
+    """A 2-D row buffer with at least `rows` rows of exactly `cols` columns
+    and unit column stride; returns its row stride."""
+    stride = _row_stride(t, name)
+    if t.shape[1] != cols:
+        raise ValueError(f"{name} rows hold {t.shape[1]} columns, the call needs {cols}")
+    if t.shape[0] < rows:
+        raise ValueError(f"{name} has {t.shape[0]} rows, the call needs {rows}")
+    return stride
+
+
+def _need_ids(expert_ids, name: str = "expert_ids", bs: Optional[int] = None, device=None):
+    _need(expert_ids, torch.int32, name, device=device)
+    if expert_ids.dim() != 2:
+        raise ValueError(f"{name} must be [BS, K]")
+    if bs is not None and expert_ids.shape[0] != bs:
+        raise ValueError(f"{name} has {expert_ids.shape[0]} rows, x has {bs}")
+    return expert_ids.shape
+
+
+def _dtype_code(out_dtype: str) -> int:
+    codes = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "e4m3": MOE_FP8_E4M3}
+    if out_dtype not in codes:
+        raise ValueError(f"out_dtype must be one of {sorted(codes)}, got {out_dtype!r}")
+    return codes[out_dtype]
+
+
 class Layout(NamedTuple):
     expert_counts: torch.Tensor   # int32 [E]
     ep_send_counts: torch.Tensor  # int32 [E+1], exclusive padded prefix, last = M_pad
     expand_idx: torch.Tensor      # int32 [BS*K], within-expert rank (-1 = dropped pair)
     status: torch.Tensor          # int32 [1], moe_flag bits
+
+
+def _layout(out: Optional[Layout], n_experts: int, n_pairs: int, device) -> Layout:
+    """The caller's Layout, checked against the call's sizes, or a new one."""
+    if out is None:
+        return Layout(torch.empty(n_experts, dtype=torch.int32, device=device),
+                      torch.empty(n_experts + 1, dtype=torch.int32, device=device),
+                      torch.empty(n_pairs, dtype=torch.int32, device=device),
+                      torch.empty(1, dtype=torch.int32, device=device))
+    for t, n, name in ((out.expert_counts, n_experts, "expert_counts"),
+                       (out.ep_send_counts, n_experts + 1, "ep_send_counts"),
+                       (out.expand_idx, n_pairs, "expand_idx"), (out.status, 1, "status")):
+        _need(t, torch.int32, f"out.{name}", device=device)
+        _need_len(t, n, f"out.{name}")
+    return out
+
+
+def _workspace(workspace: Optional[torch.Tensor], bs: int, k: int, n_experts: int, device):
+    """The caller's workspace (checked for size), or a new zero-filled one;
+    None when the layout needs none."""
+    ws_bytes = moe_dispatch_layout_workspace_size(bs, k, n_experts)
+    if workspace is None:
+        return torch.zeros(ws_bytes, dtype=torch.uint8, device=device) if ws_bytes else None
+    _need(workspace, workspace.dtype, "workspace", device=device)
+    if _nbytes(workspace) < ws_bytes:
+        raise ValueError(f"workspace holds {_nbytes(workspace)} bytes, the call needs {ws_bytes}")
+    return workspace
+
+
+def _scatter_outputs(expand_x, quant_scales, capacity_rows, bs, k, hidden, n_experts, align,
+                     dtype, device):
+    """The dispatched-row buffer (and e4m3 scales) of a scatter: the caller's,
+    checked against capacity_rows and the row size, or new ones."""
+    if capacity_rows is None:
+        capacity_rows = (expand_x.shape[0] if expand_x is not None
+                         else moe_dispatch_capacity(bs, k, n_experts, align))
+    if capacity_rows < 0:
+        raise ValueError("capacity_rows must be >= 0")
+    row_dtype = torch.bfloat16 if dtype == MOE_BF16 else torch.uint8
+    if expand_x is None:
+        expand_x = torch.empty((capacity_rows, hidden), dtype=row_dtype, device=device)
+    _need(expand_x, row_dtype, "expand_x", contiguous=False, device=device)
+    _need_rows(expand_x, capacity_rows, hidden, "expand_x")
+    if dtype == MOE_FP8_E4M3:
+        if hidden % 128:
+            raise ValueError("e4m3 output needs hidden to be a multiple of 128")
+        if quant_scales is None:
+            quant_scales = torch.empty((capacity_rows, hidden // 128), dtype=torch.float32,
+                                       device=device)
+        _need(quant_scales, torch.float32, "quant_scales", device=device)
+        _need_rows(quant_scales, capacity_rows, hidden // 128, "quant_scales")
+    return capacity_rows, expand_x, quant_scales
 
 
 def moe_dispatch_capacity(bs: int, k: int, num_experts: int, align: int = 128) -> int:
@@ -175,33 +306,50 @@ def moe_dispatch_capacity(bs: int, k: int, num_experts: int, align: int = 128) -
 
 
 def moe_dispatch_layout_workspace_size(bs: int, k: int, num_experts: int) -> int:
+    """Bytes of device workspace the layout needs (0: none).  A workspace must
+    be zero-filled before its first use; every call leaves it so."""
     return int(load_library().moe_dispatch_layout_workspace_size(bs, k, num_experts))
 
 
 def moe_dispatch_layout(expert_ids: torch.Tensor, num_experts: int, align: int = 128, *,
                         out: Optional[Layout] = None,
-                        workspace: Optional[torch.Tensor] = None) -> Layout:
-    """Counts, padded prefix and stable ranks of a [BS, K] int32 routing."""
-    _need(expert_ids, torch.int32, "expert_ids")
-    if expert_ids.dim() != 2:
-        raise ValueError("expert_ids must be [BS, K]")
-    bs, k = expert_ids.shape
+                        workspace: Optional[torch.Tensor] = None,
+                        check: bool = False) -> Layout:
+    """Counts, padded prefix and stable ranks of a [BS, K] int32 routing.
+    With check=True the call waits for the GPU and raises MoeStatusError if
+    the status word reports out-of-range or repeated ids."""
+    bs, k = _need_ids(expert_ids)
     dev = expert_ids.device
-    if out is None:
-        out = Layout(torch.empty(num_experts, dtype=torch.int32, device=dev),
-                     torch.empty(num_experts + 1, dtype=torch.int32, device=dev),
-                     torch.empty(bs * k, dtype=torch.int32, device=dev),
-                     torch.empty(1, dtype=torch.int32, device=dev))
-    ws_bytes = moe_dispatch_layout_workspace_size(bs, k, num_experts)
-    if ws_bytes and workspace is None:
-        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    out = _layout(out, num_experts, bs * k, dev)
+    workspace = _workspace(workspace, bs, k, num_experts, dev)
     rc = load_library().moe_dispatch_layout(
         _ptr(expert_ids), bs, k, num_experts, align, _ptr(out.expert_counts),
         _ptr(out.ep_send_counts), _ptr(out.expand_idx), _ptr(out.status), _ptr(workspace),
-        0 if workspace is None else workspace.numel() * workspace.element_size(),
-        _stream(expert_ids))
+        _nbytes(workspace), _stream(expert_ids))
     _check(rc)
+    if check:
+        _raise_on_status(out.status, "moe_dispatch_layout")
     return out
+
+
+def _routes(expert_ids, expand_idx, ep_send_counts, num_experts, bs, dev):
+    """The layout outputs a dispatch or combine reads, checked for size."""
+    _, k = _need_ids(expert_ids, bs=bs, device=dev)
+    _need(expand_idx, torch.int32, "expand_idx", device=dev)
+    _need_len(expand_idx, bs * k, "expand_idx")
+    _need(ep_send_counts, torch.int32, "ep_send_counts", device=dev)
+    _need_len(ep_send_counts, num_experts + 1, "ep_send_counts")
+    return k
+
+
+def _status_word(status: Optional[torch.Tensor], check: bool, dev):
+    """The in/out status word of a scatter or combine: the caller's (checked),
+    or with check=True a new zeroed one."""
+    if status is None:
+        return torch.zeros(1, dtype=torch.int32, device=dev) if check else None
+    _need(status, torch.int32, "status", device=dev)
+    _need_len(status, 1, "status")
+    return status
 
 
 def moe_dispatch(x: torch.Tensor, expert_ids: torch.Tensor, expand_idx: torch.Tensor,
@@ -209,33 +357,31 @@ def moe_dispatch(x: torch.Tensor, expert_ids: torch.Tensor, expand_idx: torch.Te
                  capacity_rows: Optional[int] = None, out_dtype: str = "bf16",
                  expand_x: Optional[torch.Tensor] = None,
                  quant_scales: Optional[torch.Tensor] = None,
-                 status: Optional[torch.Tensor] = None, align: int = 128):
+                 status: Optional[torch.Tensor] = None, align: int = 128, check: bool = False):
     """Scatter x [BS, H] bf16 into expand_x [capacity_rows, H] (bf16, or e4m3
     codes as uint8 plus fp32 scales [capacity_rows, H/128]).  Returns
-    ``expand_x`` or ``(expand_x, quant_scales)``."""
+    ``expand_x`` or ``(expand_x, quant_scales)``.  A capacity_rows below
+    moe_dispatch_capacity is allowed (a caller that knows the padded total
+    may size the buffer to it); pairs past it are dropped and flagged
+    MOE_FLAG_GUARD, which check=True turns into MoeStatusError."""
     _need(x, torch.bfloat16, "x", contiguous=False)
-    _need(expert_ids, torch.int32, "expert_ids")
-    _need(expand_idx, torch.int32, "expand_idx")
-    _need(ep_send_counts, torch.int32, "ep_send_counts")
+    dev = x.device
+    if x.dim() != 2:
+        raise ValueError("x must be [BS, H]")
     bs, hidden = x.shape
-    k = expert_ids.shape[1]
-    dtype = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "e4m3": MOE_FP8_E4M3}[out_dtype]
-    if capacity_rows is None:
-        capacity_rows = (expand_x.shape[0] if expand_x is not None
-                         else moe_dispatch_capacity(bs, k, num_experts, align))
-    if expand_x is None:
-        expand_x = torch.empty((capacity_rows, hidden),
-                               dtype=torch.bfloat16 if dtype == MOE_BF16 else torch.uint8,
-                               device=x.device)
-    if dtype == MOE_FP8_E4M3 and quant_scales is None:
-        quant_scales = torch.empty((capacity_rows, hidden // 128), dtype=torch.float32,
-                                   device=x.device)
+    k = _routes(expert_ids, expand_idx, ep_send_counts, num_experts, bs, dev)
+    dtype = _dtype_code(out_dtype)
+    capacity_rows, expand_x, quant_scales = _scatter_outputs(
+        expand_x, quant_scales, capacity_rows, bs, k, hidden, num_experts, align, dtype, dev)
+    status = _status_word(status, check, dev)
     rc = load_library().moe_dispatch(
         _ptr(x), _row_stride(x, "x"), bs, hidden, _ptr(expert_ids), _ptr(expand_idx),
         _ptr(ep_send_counts), k, num_experts, _ptr(expand_x), _row_stride(expand_x, "expand_x"),
         capacity_rows, dtype, _ptr(quant_scales) if dtype == MOE_FP8_E4M3 else None,
         _ptr(status), _stream(x))
     _check(rc)
+    if check:
+        _raise_on_status(status, "moe_dispatch")
     return expand_x if dtype == MOE_BF16 else (expand_x, quant_scales)
 
 
@@ -244,72 +390,74 @@ def moe_dispatch_fused(x: torch.Tensor, expert_ids: torch.Tensor, num_experts: i
                        capacity_rows: Optional[int] = None, out_dtype: str = "bf16",
                        expand_x: Optional[torch.Tensor] = None,
                        quant_scales: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None):
+                       workspace: Optional[torch.Tensor] = None, check: bool = False):
     """moe_dispatch_layout + moe_dispatch in one call (one launch for batches
-    of at most 2048 pairs).  Returns ``(layout, expand_x)`` or
-    ``(layout, expand_x, quant_scales)``."""
+    of at most 2048 pairs, two above).  Returns ``(layout, expand_x)`` or
+    ``(layout, expand_x, quant_scales)``.  check=True waits for the GPU and
+    raises MoeStatusError on any status bit."""
     _need(x, torch.bfloat16, "x", contiguous=False)
-    _need(expert_ids, torch.int32, "expert_ids")
-    if expert_ids.dim() != 2 or expert_ids.shape[0] != x.shape[0]:
-        raise ValueError("expert_ids must be [BS, K] with BS = x.shape[0]")
-    bs, hidden = x.shape
-    k = expert_ids.shape[1]
     dev = x.device
-    dtype = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "e4m3": MOE_FP8_E4M3}[out_dtype]
-    if out is None:
-        out = Layout(torch.empty(num_experts, dtype=torch.int32, device=dev),
-                     torch.empty(num_experts + 1, dtype=torch.int32, device=dev),
-                     torch.empty(bs * k, dtype=torch.int32, device=dev),
-                     torch.empty(1, dtype=torch.int32, device=dev))
-    if capacity_rows is None:
-        capacity_rows = (expand_x.shape[0] if expand_x is not None
-                         else moe_dispatch_capacity(bs, k, num_experts, align))
-    if expand_x is None:
-        expand_x = torch.empty((capacity_rows, hidden),
-                               dtype=torch.bfloat16 if dtype == MOE_BF16 else torch.uint8,
-                               device=dev)
-    if dtype == MOE_FP8_E4M3 and quant_scales is None:
-        quant_scales = torch.empty((capacity_rows, hidden // 128), dtype=torch.float32,
-                                   device=dev)
-    ws_bytes = moe_dispatch_layout_workspace_size(bs, k, num_experts)
-    if ws_bytes and workspace is None:
-        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    if x.dim() != 2:
+        raise ValueError("x must be [BS, H]")
+    bs, hidden = x.shape
+    _, k = _need_ids(expert_ids, bs=bs, device=dev)
+    dtype = _dtype_code(out_dtype)
+    out = _layout(out, num_experts, bs * k, dev)
+    capacity_rows, expand_x, quant_scales = _scatter_outputs(
+        expand_x, quant_scales, capacity_rows, bs, k, hidden, num_experts, align, dtype, dev)
+    workspace = _workspace(workspace, bs, k, num_experts, dev)
     rc = load_library().moe_dispatch_fused(
         _ptr(x), _row_stride(x, "x"), bs, hidden, _ptr(expert_ids), k, num_experts, align,
         _ptr(out.expert_counts), _ptr(out.ep_send_counts), _ptr(out.expand_idx),
         _ptr(expand_x), _row_stride(expand_x, "expand_x"), capacity_rows, dtype,
         _ptr(quant_scales) if dtype == MOE_FP8_E4M3 else None, _ptr(out.status),
-        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
-        _stream(x))
+        _ptr(workspace), _nbytes(workspace), _stream(x))
     _check(rc)
+    if check:
+        _raise_on_status(out.status, "moe_dispatch_fused")
     return (out, expand_x) if dtype == MOE_BF16 else (out, expand_x, quant_scales)
+
+
+def _combine_rows(shared_expert_x, out, bs, hidden, dev):
+    shared_stride = 0
+    if shared_expert_x is not None:
+        _need(shared_expert_x, torch.bfloat16, "shared_expert_x", contiguous=False, device=dev)
+        shared_stride = _need_rows(shared_expert_x, bs, hidden, "shared_expert_x")
+        if shared_expert_x.shape[0] != bs:
+            raise ValueError(f"shared_expert_x has {shared_expert_x.shape[0]} rows, BS is {bs}")
+    if out is None:
+        out = torch.empty((bs, hidden), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out", device=dev)
+    if tuple(out.shape) != (bs, hidden):
+        raise ValueError(f"out must be [{bs}, {hidden}], got {list(out.shape)}")
+    return shared_stride, out
 
 
 def moe_combine(expand_x: torch.Tensor, expert_ids: torch.Tensor, expand_idx: torch.Tensor,
                 ep_send_counts: torch.Tensor, expert_scales: torch.Tensor,
                 shared_expert_x: Optional[torch.Tensor], num_experts: int, *,
                 out: Optional[torch.Tensor] = None,
-                status: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """x_out[t] = sum_j expert_scales[t,j] * expand_x[slot(t,j)] + shared_expert_x[t]."""
+                status: Optional[torch.Tensor] = None, check: bool = False) -> torch.Tensor:
+    """x_out[t] = sum_j expert_scales[t,j] * expand_x[slot(t,j)] + shared_expert_x[t].
+    check=True waits for the GPU and raises MoeStatusError if a slot fell
+    outside expand_x (that pair contributed nothing)."""
     _need(expand_x, torch.bfloat16, "expand_x", contiguous=False)
-    _need(expert_ids, torch.int32, "expert_ids")
-    _need(expand_idx, torch.int32, "expand_idx")
-    _need(ep_send_counts, torch.int32, "ep_send_counts")
-    _need(expert_scales, torch.float32, "expert_scales")
-    bs, k = expert_ids.shape
+    dev = expand_x.device
+    bs, k = _need_ids(expert_ids, device=dev)
+    _routes(expert_ids, expand_idx, ep_send_counts, num_experts, bs, dev)
+    _need(expert_scales, torch.float32, "expert_scales", device=dev)
+    _need_len(expert_scales, bs * k, "expert_scales")
+    ys = _row_stride(expand_x, "expand_x")
     cap, hidden = expand_x.shape
-    shared_stride = 0
-    if shared_expert_x is not None:
-        _need(shared_expert_x, torch.bfloat16, "shared_expert_x", contiguous=False)
-        shared_stride = _row_stride(shared_expert_x, "shared_expert_x")
-    if out is None:
-        out = torch.empty((bs, hidden), dtype=torch.bfloat16, device=expand_x.device)
-    _need(out, torch.bfloat16, "out")
+    shared_stride, out = _combine_rows(shared_expert_x, out, bs, hidden, dev)
+    status = _status_word(status, check, dev)
     rc = load_library().moe_combine(
-        _ptr(expand_x), _row_stride(expand_x, "expand_x"), cap, _ptr(expert_ids),
-        _ptr(expand_idx), _ptr(ep_send_counts), _ptr(expert_scales), _ptr(shared_expert_x),
-        shared_stride, bs, hidden, k, num_experts, _ptr(out), _ptr(status), _stream(expand_x))
+        _ptr(expand_x), ys, cap, _ptr(expert_ids), _ptr(expand_idx), _ptr(ep_send_counts),
+        _ptr(expert_scales), _ptr(shared_expert_x), shared_stride, bs, hidden, k, num_experts,
+        _ptr(out), _ptr(status), _stream(expand_x))
     _check(rc)
+    if check:
+        _raise_on_status(status, "moe_combine")
     return out
 
 
@@ -317,33 +465,47 @@ def moe_combine_fp8(expand_x: torch.Tensor, quant_scales: torch.Tensor, expert_i
                     expand_idx: torch.Tensor, ep_send_counts: torch.Tensor,
                     expert_scales: torch.Tensor, shared_expert_x: Optional[torch.Tensor],
                     num_experts: int, *, out: Optional[torch.Tensor] = None,
-                    status: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    status: Optional[torch.Tensor] = None, check: bool = False) -> torch.Tensor:
     """Combine over e4m3 expert rows (uint8 codes [cap, H]) with fp32 scales
     [cap, H/128], each term dequantised before the weighted sum."""
     _need(expand_x, torch.uint8, "expand_x", contiguous=False)
-    _need(quant_scales, torch.float32, "quant_scales")
-    _need(expert_ids, torch.int32, "expert_ids")
-    _need(expand_idx, torch.int32, "expand_idx")
-    _need(ep_send_counts, torch.int32, "ep_send_counts")
-    _need(expert_scales, torch.float32, "expert_scales")
-    bs, k = expert_ids.shape
+    dev = expand_x.device
+    bs, k = _need_ids(expert_ids, device=dev)
+    _routes(expert_ids, expand_idx, ep_send_counts, num_experts, bs, dev)
+    _need(expert_scales, torch.float32, "expert_scales", device=dev)
+    _need_len(expert_scales, bs * k, "expert_scales")
+    ys = _row_stride(expand_x, "expand_x")
     cap, hidden = expand_x.shape
-    if quant_scales.shape != (cap, hidden // 128):
+    if hidden % 128:
+        raise ValueError("e4m3 rows need hidden to be a multiple of 128")
+    _need(quant_scales, torch.float32, "quant_scales", device=dev)
+    if tuple(quant_scales.shape) != (cap, hidden // 128):
         raise ValueError("quant_scales must be [capacity_rows, hidden/128]")
-    shared_stride = 0
-    if shared_expert_x is not None:
-        _need(shared_expert_x, torch.bfloat16, "shared_expert_x", contiguous=False)
-        shared_stride = _row_stride(shared_expert_x, "shared_expert_x")
-    if out is None:
-        out = torch.empty((bs, hidden), dtype=torch.bfloat16, device=expand_x.device)
-    _need(out, torch.bfloat16, "out")
+    shared_stride, out = _combine_rows(shared_expert_x, out, bs, hidden, dev)
+    status = _status_word(status, check, dev)
     rc = load_library().moe_combine_fp8(
-        _ptr(expand_x), _row_stride(expand_x, "expand_x"), cap, _ptr(quant_scales),
-        _ptr(expert_ids), _ptr(expand_idx), _ptr(ep_send_counts), _ptr(expert_scales),
-        _ptr(shared_expert_x), shared_stride, bs, hidden, k, num_experts, _ptr(out),
-        _ptr(status), _stream(expand_x))
+        _ptr(expand_x), ys, cap, _ptr(quant_scales), _ptr(expert_ids), _ptr(expand_idx),
+        _ptr(ep_send_counts), _ptr(expert_scales), _ptr(shared_expert_x), shared_stride, bs,
+        hidden, k, num_experts, _ptr(out), _ptr(status), _stream(expand_x))
     _check(rc)
+    if check:
+        _raise_on_status(status, "moe_combine_fp8")
     return out
+
+
+def _replica_tables(replica_offsets, replica_thresholds, num_experts, dev):
+    _need(replica_offsets, torch.int32, "replica_offsets", device=dev)
+    _need_len(replica_offsets, num_experts + 1, "replica_offsets")
+    _need(replica_thresholds, (torch.int32, torch.uint32), "replica_thresholds", device=dev)
+    return replica_thresholds.numel()
+
+
+def _replica_ids(replica_ids, bs, k, dev):
+    if replica_ids is None:
+        return torch.empty((bs, k), dtype=torch.int32, device=dev)
+    _need(replica_ids, torch.int32, "replica_ids", device=dev)
+    _need_len(replica_ids, bs * k, "replica_ids")
+    return replica_ids
 
 
 def moe_dispatch_layout_replicated(expert_ids: torch.Tensor, num_experts: int,
@@ -351,35 +513,25 @@ def moe_dispatch_layout_replicated(expert_ids: torch.Tensor, num_experts: int,
                                    replica_thresholds: torch.Tensor, seed: int,
                                    align: int = 128, *, out: Optional[Layout] = None,
                                    replica_ids: Optional[torch.Tensor] = None,
-                                   workspace: Optional[torch.Tensor] = None):
+                                   workspace: Optional[torch.Tensor] = None,
+                                   check: bool = False):
     """Choose a physical replica per pair (SplitMix64 draw against cumulative
     uint32 thresholds, given as int32 or uint32 bit patterns) and lay the
     pairs out over the replicas.  Returns ``(replica_ids [BS, K], Layout)``."""
-    _need(expert_ids, torch.int32, "expert_ids")
-    _need(replica_offsets, torch.int32, "replica_offsets")
-    if replica_thresholds.dtype not in (torch.int32, torch.uint32):
-        raise ValueError("replica_thresholds must hold uint32 bit patterns (int32 or uint32)")
-    _need(replica_thresholds, replica_thresholds.dtype, "replica_thresholds")
-    bs, k = expert_ids.shape
-    p = replica_thresholds.numel()
+    bs, k = _need_ids(expert_ids)
     dev = expert_ids.device
-    if out is None:
-        out = Layout(torch.empty(p, dtype=torch.int32, device=dev),
-                     torch.empty(p + 1, dtype=torch.int32, device=dev),
-                     torch.empty(bs * k, dtype=torch.int32, device=dev),
-                     torch.empty(1, dtype=torch.int32, device=dev))
-    if replica_ids is None:
-        replica_ids = torch.empty((bs, k), dtype=torch.int32, device=dev)
-    ws_bytes = moe_dispatch_layout_workspace_size(bs, k, p)
-    if ws_bytes and workspace is None:
-        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    p = _replica_tables(replica_offsets, replica_thresholds, num_experts, dev)
+    out = _layout(out, p, bs * k, dev)
+    replica_ids = _replica_ids(replica_ids, bs, k, dev)
+    workspace = _workspace(workspace, bs, k, p, dev)
     rc = load_library().moe_dispatch_layout_replicated(
         _ptr(expert_ids), bs, k, num_experts, _ptr(replica_offsets), _ptr(replica_thresholds), p,
         seed & 0xFFFFFFFFFFFFFFFF, align, _ptr(replica_ids), _ptr(out.expert_counts),
         _ptr(out.ep_send_counts), _ptr(out.expand_idx), _ptr(out.status), _ptr(workspace),
-        0 if workspace is None else workspace.numel() * workspace.element_size(),
-        _stream(expert_ids))
+        _nbytes(workspace), _stream(expert_ids))
     _check(rc)
+    if check:
+        _raise_on_status(out.status, "moe_dispatch_layout_replicated")
     return replica_ids, out
 
 
@@ -391,52 +543,34 @@ def moe_dispatch_fused_replicated(x: torch.Tensor, expert_ids: torch.Tensor, num
                                   capacity_rows: Optional[int] = None, out_dtype: str = "bf16",
                                   expand_x: Optional[torch.Tensor] = None,
                                   quant_scales: Optional[torch.Tensor] = None,
-                                  workspace: Optional[torch.Tensor] = None):
+                                  workspace: Optional[torch.Tensor] = None,
+                                  check: bool = False):
     """moe_dispatch_layout_replicated + moe_dispatch over the replicas in one
     call.  Returns ``(replica_ids, layout, expand_x)`` or ``(replica_ids,
     layout, expand_x, quant_scales)``."""
     _need(x, torch.bfloat16, "x", contiguous=False)
-    _need(expert_ids, torch.int32, "expert_ids")
-    _need(replica_offsets, torch.int32, "replica_offsets")
-    if replica_thresholds.dtype not in (torch.int32, torch.uint32):
-        raise ValueError("replica_thresholds must hold uint32 bit patterns (int32 or uint32)")
-    _need(replica_thresholds, replica_thresholds.dtype, "replica_thresholds")
-    if expert_ids.dim() != 2 or expert_ids.shape[0] != x.shape[0]:
-        raise ValueError("expert_ids must be [BS, K] with BS = x.shape[0]")
-    bs, hidden = x.shape
-    k = expert_ids.shape[1]
-    p = replica_thresholds.numel()
     dev = x.device
-    dtype = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "e4m3": MOE_FP8_E4M3}[out_dtype]
-    if out is None:
-        out = Layout(torch.empty(p, dtype=torch.int32, device=dev),
-                     torch.empty(p + 1, dtype=torch.int32, device=dev),
-                     torch.empty(bs * k, dtype=torch.int32, device=dev),
-                     torch.empty(1, dtype=torch.int32, device=dev))
-    if replica_ids is None:
-        replica_ids = torch.empty((bs, k), dtype=torch.int32, device=dev)
-    if capacity_rows is None:
-        capacity_rows = (expand_x.shape[0] if expand_x is not None
-                         else moe_dispatch_capacity(bs, k, p, align))
-    if expand_x is None:
-        expand_x = torch.empty((capacity_rows, hidden),
-                               dtype=torch.bfloat16 if dtype == MOE_BF16 else torch.uint8,
-                               device=dev)
-    if dtype == MOE_FP8_E4M3 and quant_scales is None:
-        quant_scales = torch.empty((capacity_rows, hidden // 128), dtype=torch.float32,
-                                   device=dev)
-    ws_bytes = moe_dispatch_layout_workspace_size(bs, k, p)
-    if ws_bytes and workspace is None:
-        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    if x.dim() != 2:
+        raise ValueError("x must be [BS, H]")
+    bs, hidden = x.shape
+    _, k = _need_ids(expert_ids, bs=bs, device=dev)
+    p = _replica_tables(replica_offsets, replica_thresholds, num_experts, dev)
+    dtype = _dtype_code(out_dtype)
+    out = _layout(out, p, bs * k, dev)
+    replica_ids = _replica_ids(replica_ids, bs, k, dev)
+    capacity_rows, expand_x, quant_scales = _scatter_outputs(
+        expand_x, quant_scales, capacity_rows, bs, k, hidden, p, align, dtype, dev)
+    workspace = _workspace(workspace, bs, k, p, dev)
     rc = load_library().moe_dispatch_fused_replicated(
         _ptr(x), _row_stride(x, "x"), bs, hidden, _ptr(expert_ids), k, num_experts,
         _ptr(replica_offsets), _ptr(replica_thresholds), p, seed & 0xFFFFFFFFFFFFFFFF, align,
         _ptr(replica_ids), _ptr(out.expert_counts), _ptr(out.ep_send_counts),
         _ptr(out.expand_idx), _ptr(expand_x), _row_stride(expand_x, "expand_x"), capacity_rows,
         dtype, _ptr(quant_scales) if dtype == MOE_FP8_E4M3 else None, _ptr(out.status),
-        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
-        _stream(x))
+        _ptr(workspace), _nbytes(workspace), _stream(x))
     _check(rc)
+    if check:
+        _raise_on_status(out.status, "moe_dispatch_fused_replicated")
     if dtype == MOE_BF16:
         return replica_ids, out, expand_x
     return replica_ids, out, expand_x, quant_scales
@@ -445,29 +579,25 @@ def moe_dispatch_fused_replicated(x: torch.Tensor, expert_ids: torch.Tensor, num
 def moe_dispatch_layout_ep(expert_ids: torch.Tensor, num_experts: int, ep_world_size: int,
                            align: int = 128, *, out: Optional[Layout] = None,
                            rank_offsets: Optional[torch.Tensor] = None,
-                           workspace: Optional[torch.Tensor] = None):
+                           workspace: Optional[torch.Tensor] = None, check: bool = False):
     """The layout plus per-destination-rank send offsets (experts split evenly
     and contiguously over ``ep_world_size`` ranks).  Returns
     ``(Layout, rank_offsets int32 [ws+1])``."""
-    _need(expert_ids, torch.int32, "expert_ids")
-    bs, k = expert_ids.shape
+    bs, k = _need_ids(expert_ids)
     dev = expert_ids.device
-    if out is None:
-        out = Layout(torch.empty(num_experts, dtype=torch.int32, device=dev),
-                     torch.empty(num_experts + 1, dtype=torch.int32, device=dev),
-                     torch.empty(bs * k, dtype=torch.int32, device=dev),
-                     torch.empty(1, dtype=torch.int32, device=dev))
+    out = _layout(out, num_experts, bs * k, dev)
     if rank_offsets is None:
         rank_offsets = torch.empty(max(ep_world_size, 0) + 1, dtype=torch.int32, device=dev)
-    ws_bytes = moe_dispatch_layout_workspace_size(bs, k, num_experts)
-    if ws_bytes and workspace is None:
-        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    _need(rank_offsets, torch.int32, "rank_offsets", device=dev)
+    _need_len(rank_offsets, max(ep_world_size, 0) + 1, "rank_offsets")
+    workspace = _workspace(workspace, bs, k, num_experts, dev)
     rc = load_library().moe_dispatch_layout_ep(
         _ptr(expert_ids), bs, k, num_experts, ep_world_size, align, _ptr(out.expert_counts),
         _ptr(out.ep_send_counts), _ptr(rank_offsets), _ptr(out.expand_idx), _ptr(out.status),
-        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
-        _stream(expert_ids))
+        _ptr(workspace), _nbytes(workspace), _stream(expert_ids))
     _check(rc)
+    if check:
+        _raise_on_status(out.status, "moe_dispatch_layout_ep")
     return out, rank_offsets
 
 
@@ -501,7 +631,7 @@ def moe_probe_stream_mix(src: torch.Tensor, dst: torch.Tensor, items: int, reads
     tensors whose rows are the probe's rows; src_rows / dst_rows optional
     int32 row indices."""
     for t, name in ((src, "src"), (dst, "dst")):
-        if not t.is_cuda or t.dim() != 2 or not t.is_contiguous():
+        if t.device.type != _DEVICE_TYPE or t.dim() != 2 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous 2-D device tensor")
     row_bytes = src.shape[1] * src.element_size()
     if dst.shape[1] * dst.element_size() != row_bytes:

@@ -151,11 +151,11 @@ __global__ __launch_bounds__(THREADS) void dispatch_fp8_kernel(
 int kmax_for(int32_t k) { return k <= 2 ? 2 : k <= 4 ? 4 : k <= 8 ? 8 : 16; }
 
 // Launch shape of the bf16 scatter.  With the token rows already in the
-// Infinity Cache (read ahead by the layout launches), the scatter is bound
-// by its row writes alone, and HBM takes them faster from fewer waves in
-// flight, which write a narrower window of destination rows: 64-thread
-// workgroups holding 19 KB of LDS each, so that at most 8 share a compute
-// unit (2 waves per SIMD).  Rows that still come from HBM need the latency
+// Infinity Cache (read ahead by the layout's ranking launch), the scatter is
+// bound by its row writes alone, and HBM takes them faster from fewer waves
+// in flight, which write a narrower window of destination rows: 64-thread
+// workgroups holding enough LDS that at most 7 share a compute unit (under 2
+// waves per SIMD).  Rows that still come from HBM need the latency
 // hiding of full occupancy, so they keep 128-thread workgroups with only
 // the send counts in LDS.
 template <int THREADS, int LDS_INTS, bool DEFER>
@@ -237,8 +237,14 @@ hipError_t launch_fp8_shape(const void* x, int64_t x_stride, int32_t bs, int32_t
   return hipGetLastError();
 }
 
+#ifndef MOE_CACHED_ROWS_PER_CU
+#define MOE_CACHED_ROWS_PER_CU 7   // workgroups of the cache-resident scatter per compute unit
+#endif
 constexpr int kCachedRowsThreads = 64;
-constexpr int kCachedRowsLdsInts = 19456 / 4;  // 8 workgroups in a compute unit's 160 KB
+// LDS per workgroup such that MOE_CACHED_ROWS_PER_CU fit a compute unit's
+// 160 KB and one more does not (in 512-byte steps).
+constexpr int kCachedRowsLdsInts = (163840 / MOE_CACHED_ROWS_PER_CU) / 512 * 512 / 4;
+static_assert((MOE_CACHED_ROWS_PER_CU + 1) * kCachedRowsLdsInts * 4 > 163840, "cap");
 
 }  // namespace
 

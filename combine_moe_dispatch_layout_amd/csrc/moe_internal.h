@@ -304,7 +304,10 @@ struct ReadAhead {
 #endif
 constexpr bool kFusedDefer = MOE_FUSED_DEFER != 0;
 constexpr int kReadAheadRankPercent = MOE_READ_AHEAD_RANK_PERCENT;
-constexpr int kReadAheadMaxBlocks = 240;  // of the 256 compute units, with the ranking workgroups
+#ifndef MOE_READ_AHEAD_BLOCKS
+#define MOE_READ_AHEAD_BLOCKS 240  // of the 256 compute units, with the ranking workgroups
+#endif
+constexpr int kReadAheadMaxBlocks = MOE_READ_AHEAD_BLOCKS;
 constexpr int64_t kReadAheadMaxBytes = int64_t(128) << 20;
 constexpr int kReadAheadUnroll = 16;      // loads in flight per thread
 

@@ -227,8 +227,13 @@ int moe_dispatch_layout_replicated(const int32_t* expert_ids, int32_t bs, int32_
  *                     bytes a multiple of 16.  Row slot(t,j) receives token t
  *                     for every pair j.  Padding rows are NOT written.
  *  capacity_rows  in  rows of expand_x (size it with moe_dispatch_capacity).
- *                     With 0 rows every pair is guarded and nothing is
- *                     written; expand_x and quant_scales may then be NULL.
+ *                     A smaller value is accepted (a caller that knows the
+ *                     padded total may size the buffer to it), but a pair
+ *                     whose row lies at or beyond capacity_rows is DROPPED:
+ *                     its row is not written and MOE_FLAG_GUARD is set in
+ *                     `status`, which such a caller must read.  With 0 rows
+ *                     every pair is guarded and nothing is written; expand_x
+ *                     and quant_scales may then be NULL.
  *  quant_scales   out fp32 [capacity_rows, hidden/128] row-major when
  *                     out_dtype is MOE_FP8_E4M3 (else ignored, may be NULL):
  *                     s = amax/448 over the 128 channels of the block;
@@ -301,7 +306,9 @@ int moe_dispatch_fused(const void* x, int64_t x_stride, int32_t bs, int32_t hidd
  *  bs, hidden     in  as for moe_dispatch (bs*hidden/8 < 2^31).
  *  x_out          out bf16 [bs, hidden], contiguous (the page requires a
  *                     contiguous output), 16-byte aligned.
- *  status         in/out int32 [1] or NULL: MOE_FLAG_GUARD OR-ed in as above.
+ *  status         in/out int32 [1] or NULL: MOE_FLAG_GUARD is OR-ed in when a
+ *                     pair's row lies at or beyond capacity_rows; that pair
+ *                     contributes nothing to its token's sum.
  */
 int moe_combine(const void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
                 const int32_t* expert_ids, const int32_t* expand_idx,
