@@ -431,10 +431,16 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 }  // namespace
 
+// Workspace layout: the arrival counter in the first 256 bytes, at the same
+// place for every shape (so a workspace reused for batches of other shapes
+// still holds a zero counter there), then the histograms, the flags and the
+// ranks within the workgroups.
+constexpr size_t kCounterBytes = 256;
+
 size_t layout_workspace_bytes(const LayoutPlan& p, int32_t num_experts) {
   if (p.blocks <= 1) return 0;
-  return align256((size_t)p.blocks * num_experts * sizeof(int32_t)) +
-         align256((size_t)p.blocks * sizeof(int32_t)) + 256 +
+  return kCounterBytes + align256((size_t)p.blocks * num_experts * sizeof(int32_t)) +
+         align256((size_t)p.blocks * sizeof(int32_t)) +
          align256((size_t)p.n_pairs * sizeof(int32_t));
 }
 
@@ -444,10 +450,10 @@ LayoutScratch layout_scratch(const LayoutPlan& p, int32_t num_experts, void* wor
   char* base = static_cast<char*>(workspace);
   const size_t hist = align256((size_t)p.blocks * num_experts * sizeof(int32_t));
   const size_t flags = align256((size_t)p.blocks * sizeof(int32_t));
-  ws.hist = reinterpret_cast<int32_t*>(base);
-  ws.flags = reinterpret_cast<int32_t*>(base + hist);
-  ws.arrivals = reinterpret_cast<int32_t*>(base + hist + flags);
-  ws.ranks = reinterpret_cast<int32_t*>(base + hist + flags + 256);
+  ws.arrivals = reinterpret_cast<int32_t*>(base);
+  ws.hist = reinterpret_cast<int32_t*>(base + kCounterBytes);
+  ws.flags = reinterpret_cast<int32_t*>(base + kCounterBytes + hist);
+  ws.ranks = reinterpret_cast<int32_t*>(base + kCounterBytes + hist + flags);
   return ws;
 }
 

@@ -244,8 +244,9 @@ constexpr int kLayoutSingleMaxRounds = MOE_LAYOUT_SINGLE_ROUNDS;
 constexpr int kLayoutMultiRounds = MOE_LAYOUT_MULTI_ROUNDS;
 constexpr int kLayoutMaxBlocks = 256;
 
-// The multi-workgroup layout's device workspace.  `arrivals` must be zero
-// when a call starts; every call leaves it zero again.
+// The multi-workgroup layout's device workspace.  `arrivals` (always the
+// workspace's first word) must be zero when a call starts; every call leaves
+// it zero again.  The rest needs no initial contents.
 struct LayoutScratch {
   int32_t* hist = nullptr;      // [blocks][E] histograms, then their column prefix
   int32_t* flags = nullptr;     // [blocks] status bits per workgroup

@@ -93,10 +93,12 @@ int64_t moe_dispatch_capacity(int32_t bs, int32_t k, int32_t num_experts, int32_
  * invalid arguments as well; the layout call reports those.
  * The workspace must be zero-filled before its first use (for example with
  * hipMemset, or a fill kernel where a memset node is unwanted, as under
- * graph capture); every call returns it to that state when its kernels
- * finish.  It holds the ranking workgroups' histograms, which the last
- * workgroup to finish scans, and the arrival counter that tells a workgroup
- * it is the last. */
+ * graph capture).  Its first word is an arrival counter that tells a ranking
+ * workgroup it is the last to finish; every call leaves that word zero
+ * again, so one workspace serves any number of calls of any shapes that fit
+ * it, one call at a time.  The rest (the ranking workgroups' histograms,
+ * which the last workgroup scans, their flags and ranks) needs no initial
+ * contents. */
 size_t moe_dispatch_layout_workspace_size(int32_t bs, int32_t k, int32_t num_experts);
 
 /*

@@ -802,3 +802,46 @@ def test_layout_largest_batch():
     ids = rotated_ids(rng, bs, e, k)
     (c, s, r, f), _ = assert_layout_equal(ids, e, align)
     assert int(c.sum()) == bs * k and f == 0
+
+
+def sentinel_layout(e, n):
+    """Layout outputs filled with -7, so that an output a call fails to
+    write cannot pass by holding an earlier call's values."""
+    moe = moe_mod()
+    return moe.Layout(*(torch.full((m,), -7, dtype=torch.int32, device=DEV)
+                        for m in (e, e + 1, n, 1)))
+
+
+def test_workspace_reused_across_shapes():
+    """One caller workspace, zero-filled once, serves a run of layout and
+    fused calls of changing shapes (multi-workgroup and one-launch), each
+    bit-exact against the oracle; the arrival counter, the workspace's first
+    word, is zero after every call."""
+    moe = moe_mod()
+    rng = np.random.default_rng(107)
+    shapes = [(3000, 256, 8), (700, 64, 6), (100, 64, 8), (4096, 256, 8), (20000, 512, 16),
+              (600, 17, 3), (70000, 1, 1), (4096, 256, 8)]
+    size = max(moe.moe_dispatch_layout_workspace_size(bs, k, e) for bs, e, k in shapes)
+    ws = torch.zeros(size, dtype=torch.uint8, device=DEV)
+    h = 128
+    for i, (bs, e, k) in enumerate(shapes):
+        ids = random_ids(rng, bs, e, k)
+        c, s, r, f = oracle.layout(ids, e, 128)
+        lay = moe.moe_dispatch_layout(dev(ids), e, 128, out=sentinel_layout(e, bs * k),
+                                      workspace=ws)
+        x = random_bf16(rng, (bs, h))
+        cap = oracle.capacity(bs, k, e, 128)
+        rows = torch.full((cap, h), oracle.SENTINEL_BF16, dtype=torch.int16,
+                          device=DEV).view(torch.bfloat16)
+        fused, _ = moe.moe_dispatch_fused(bf16_dev(x), dev(ids), e, 128,
+                                          out=sentinel_layout(e, bs * k), capacity_rows=cap,
+                                          expand_x=rows, workspace=ws)
+        torch.cuda.synchronize()
+        for got in (lay, fused):
+            np.testing.assert_array_equal(got.expert_counts.cpu().numpy(), c, err_msg=str(i))
+            np.testing.assert_array_equal(got.ep_send_counts.cpu().numpy(), s, err_msg=str(i))
+            np.testing.assert_array_equal(got.expand_idx.cpu().numpy(), r, err_msg=str(i))
+            assert int(got.status.cpu()[0]) == f
+        np.testing.assert_array_equal(host_bits(rows),
+                                      oracle.dispatch_bf16(x, ids, r, s, e, cap)[0])
+        assert int(ws[:4].view(torch.int32)[0]) == 0
