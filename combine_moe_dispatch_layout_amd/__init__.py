@@ -59,6 +59,7 @@ __all__ = [
     "moe_dispatch_capacity", "moe_dispatch_layout_workspace_size",
     "moe_dispatch_layout", "moe_dispatch_layout_ep", "moe_dispatch_layout_replicated",
     "moe_dispatch", "moe_dispatch_fused", "moe_dispatch_fused_replicated", "moe_combine",
+    "moe_dispatch_fused_noalloc", "moe_noalloc_scratch_bytes",
     "moe_plan_compensation",
     "moe_combine_fp8", "moe_probe_stream_mix", "moe_time_next_launches",
     "moe_time_unused_launches",
@@ -68,7 +69,8 @@ __all__ = [
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmoe_dispatch.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = range(5)
+(MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP,
+ MOE_ERR_SCRATCH) = range(6)
 MOE_BF16, MOE_FP8_E4M3 = 0, 1
 MOE_FLAG_ID_RANGE, MOE_FLAG_DUP_ID, MOE_FLAG_GUARD, MOE_FLAG_REPLICA = 1, 2, 4, 8
 
@@ -106,6 +108,9 @@ def load_library() -> ctypes.CDLL:
                                         P, P, P]),
         "moe_dispatch_fused": (ctypes.c_int, [P, i64, i32, i32, P, i32, i32, i32, P, P, P, P,
                                               i64, i64, i32, P, P, P, sz, P]),
+        "moe_dispatch_fused_noalloc": (ctypes.c_int, [P, i64, i32, i32, P, i32, i32, i32, P,
+                                                      P, P, P, i64, i64, i32, P, P, P]),
+        "moe_noalloc_scratch_bytes": (sz, []),
         "moe_combine": (ctypes.c_int, [P, i64, i64, P, P, P, P, P, i64, i32, i32, i32, i32, P,
                                        P, P]),
         "moe_combine_fp8": (ctypes.c_int, [P, i64, i64, P, P, P, P, P, P, i64, i32, i32, i32,
@@ -416,6 +421,43 @@ def moe_dispatch_fused(x: torch.Tensor, expert_ids: torch.Tensor, num_experts: i
     if check:
         _raise_on_status(out.status, "moe_dispatch_fused")
     return (out, expand_x) if dtype == MOE_BF16 else (out, expand_x, quant_scales)
+
+
+def moe_dispatch_fused_noalloc(x: torch.Tensor, expert_ids: torch.Tensor, num_experts: int,
+                               align: int = 128, *, out: Optional[Layout] = None,
+                               capacity_rows: Optional[int] = None, out_dtype: str = "bf16",
+                               expand_x: Optional[torch.Tensor] = None,
+                               quant_scales: Optional[torch.Tensor] = None,
+                               check: bool = False):
+    """moe_dispatch_fused with the layout's workspace in the library's static
+    per-GPU scratch (no device allocation by the call; pass `out`,
+    `expand_x` and, for e4m3, `quant_scales` to allocate nothing at all).
+    Batches whose workspace exceeds moe_noalloc_scratch_bytes() raise
+    MoeError (MOE_ERR_SCRATCH).  Calls that overlap on one GPU race."""
+    _need(x, torch.bfloat16, "x", contiguous=False)
+    dev = x.device
+    if x.dim() != 2:
+        raise ValueError("x must be [BS, H]")
+    bs, hidden = x.shape
+    _, k = _need_ids(expert_ids, bs=bs, device=dev)
+    dtype = _dtype_code(out_dtype)
+    out = _layout(out, num_experts, bs * k, dev)
+    capacity_rows, expand_x, quant_scales = _scatter_outputs(
+        expand_x, quant_scales, capacity_rows, bs, k, hidden, num_experts, align, dtype, dev)
+    rc = load_library().moe_dispatch_fused_noalloc(
+        _ptr(x), _row_stride(x, "x"), bs, hidden, _ptr(expert_ids), k, num_experts, align,
+        _ptr(out.expert_counts), _ptr(out.ep_send_counts), _ptr(out.expand_idx),
+        _ptr(expand_x), _row_stride(expand_x, "expand_x"), capacity_rows, dtype,
+        _ptr(quant_scales) if dtype == MOE_FP8_E4M3 else None, _ptr(out.status), _stream(x))
+    _check(rc)
+    if check:
+        _raise_on_status(out.status, "moe_dispatch_fused_noalloc")
+    return (out, expand_x) if dtype == MOE_BF16 else (out, expand_x, quant_scales)
+
+
+def moe_noalloc_scratch_bytes() -> int:
+    """Bytes of the static per-GPU scratch of moe_dispatch_fused_noalloc."""
+    return int(load_library().moe_noalloc_scratch_bytes())
 
 
 def _combine_rows(shared_expert_x, out, bs, hidden, dev):

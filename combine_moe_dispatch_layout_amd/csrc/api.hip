@@ -158,6 +158,8 @@ const char* moe_status_string(int status) {
     case MOE_ERR_WORKSPACE: return "workspace smaller than moe_dispatch_layout_workspace_size";
     case MOE_ERR_UNSUPPORTED: return "unsupported dtype";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_SCRATCH:
+      return "batch needs more than the no-allocation entry point's static scratch";
     default: return "unknown status";
   }
 }

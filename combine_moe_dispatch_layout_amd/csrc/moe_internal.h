@@ -304,6 +304,11 @@ struct ReadAhead {
 #define MOE_READ_AHEAD_RANK_PERCENT 60
 #endif
 constexpr bool kFusedDefer = MOE_FUSED_DEFER != 0;
+// Static scratch of moe_dispatch_fused_noalloc, per GPU: enough for the
+// layout workspace of any batch of at most 2^20 pairs (E <= 512).
+#ifndef MOE_NOALLOC_SCRATCH_BYTES
+#define MOE_NOALLOC_SCRATCH_BYTES (size_t(5) << 20)
+#endif
 constexpr int kReadAheadRankPercent = MOE_READ_AHEAD_RANK_PERCENT;
 #ifndef MOE_READ_AHEAD_BLOCKS
 #define MOE_READ_AHEAD_BLOCKS 240  // of the 256 compute units, with the ranking workgroups

@@ -51,7 +51,8 @@ enum moe_status {
     MOE_ERR_INVALID_ARG = 1,   /* a shape, range, pointer or alignment rule failed */
     MOE_ERR_WORKSPACE = 2,     /* workspace_bytes below moe_dispatch_layout_workspace_size */
     MOE_ERR_UNSUPPORTED = 3,   /* unknown dtype */
-    MOE_ERR_HIP = 4            /* the HIP runtime refused a launch */
+    MOE_ERR_HIP = 4,           /* the HIP runtime refused a launch */
+    MOE_ERR_SCRATCH = 5        /* batch too large for moe_dispatch_fused_noalloc's scratch */
 };
 
 /* Element type of the dispatched buffer. */
@@ -287,6 +288,31 @@ int moe_dispatch_fused(const void* x, int64_t x_stride, int32_t bs, int32_t hidd
                        void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
                        int32_t out_dtype, float* quant_scales, int32_t* status, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * moe_dispatch_fused without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing; the layout's
+ * workspace is a static device array of moe_noalloc_scratch_bytes() bytes
+ * (5 MiB) that each GPU the library runs on holds until the process ends,
+ * its address looked up once per device on the first call there.  Every
+ * batch of at most 2^20 pairs fits (more with fewer experts: the rule is
+ * moe_dispatch_layout_workspace_size(bs, k, num_experts) <=
+ * moe_noalloc_scratch_bytes()); a larger one returns MOE_ERR_SCRATCH and
+ * enqueues nothing.  All calls on one GPU share its array: calls that
+ * overlap on one GPU (from other streams or threads) race and must be
+ * serialised by the caller.  Arguments, outputs and results are those of
+ * moe_dispatch_fused, bit for bit.
+ */
+int moe_dispatch_fused_noalloc(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
+                               const int32_t* expert_ids, int32_t k, int32_t num_experts,
+                               int32_t align, int32_t* expert_counts, int32_t* ep_send_counts,
+                               int32_t* expand_idx, void* expand_x, int64_t expand_x_stride,
+                               int64_t capacity_rows, int32_t out_dtype, float* quant_scales,
+                               int32_t* status, void* stream);
+
+/* Bytes of the static per-GPU scratch moe_dispatch_fused_noalloc uses. */
+size_t moe_noalloc_scratch_bytes(void);
 
 /*
  * Combine: gather each token's K expert-output rows back and form

@@ -255,6 +255,28 @@ def test_dispatch_fused_rules(lib):
     assert call(bs=4096, k=8, e=256) == 2
 
 
+def test_dispatch_fused_noalloc_rules(lib):
+    """The no-allocation entry point refuses, before any HIP call, a batch
+    whose layout workspace exceeds its static scratch, and otherwise applies
+    moe_dispatch_fused's argument rules."""
+    lib.moe_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    scratch = lib.moe_noalloc_scratch_bytes()
+    assert scratch == 5 << 20
+    assert lib.moe_dispatch_layout_workspace_size((1 << 20) // 8, 8, 512) <= scratch
+
+    def call(bs=4, k=2, e=8, dtype=0, cap=64, counts=FAKE):
+        return lib.moe_dispatch_fused_noalloc(FAKE, 64, bs, 64, FAKE, k, e, 128, counts, FAKE,
+                                              FAKE, FAKE, 64, cap, dtype, None, None, None)
+
+    assert lib.moe_dispatch_layout_workspace_size(170000, 8, 512) > scratch
+    assert call(bs=170000, k=8, e=512) == 5   # beyond the scratch
+    assert lib.moe_status_string(5).decode().startswith("batch needs more")
+    assert call(dtype=5) == 3                  # then the fused call's own rules
+    assert call(k=9) == 1
+    assert call(counts=None) == 1
+    assert call(cap=-1) == 1
+
+
 def test_probe_rules(lib):
     def call(items=4, row_bytes=64, reads=1, writes=8, src_total=4, dst_total=32, src=FAKE,
              dst=FAKE, src_rows=None, dst_rows=None):
