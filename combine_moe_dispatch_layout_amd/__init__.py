@@ -177,7 +177,7 @@ _DEVICE_TYPE = "cuda"
 
 def _stream(t: torch.Tensor) -> Optional[int]:
     if _raw_stream is not None:
-        return _raw_stream(t.device.index)
+        return _raw_stream(t.get_device())
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
@@ -189,20 +189,40 @@ def _nbytes(t: Optional[torch.Tensor]) -> int:
     return 0 if t is None else t.numel() * t.element_size()
 
 
-def _need(t, dtype, name: str, contiguous: bool = True, device=None) -> None:
-    """t is a tensor of `dtype` (a dtype or a tuple of them) on the library's
-    device type (and on `device` when given), contiguous unless told not."""
-    if not isinstance(t, torch.Tensor):
-        raise ValueError(f"{name} must be a tensor")
-    if t.device.type != _DEVICE_TYPE:
+# The checks read each tensor's facts once through torch's cheapest
+# accessors (get_device() rather than .device): a decode-sized step is
+# bound by host time, and these run on every call.
+
+def _device_of(t, name: str) -> int:
+    """The device index of a tensor argument (-1 on the CPU test tier)."""
+    try:
+        dev = t.get_device()
+    except AttributeError:
+        raise ValueError(f"{name} must be a tensor") from None
+    if (dev >= 0) != (_DEVICE_TYPE == "cuda"):
         raise ValueError(f"{name} must be a device tensor")
-    if device is not None and t.device != device:
-        raise ValueError(f"{name} is on {t.device}, the call's tensors on {device}")
-    dtypes = dtype if isinstance(dtype, tuple) else (dtype,)
-    if t.dtype not in dtypes:
-        raise ValueError(f"{name} must be {' or '.join(map(str, dtypes))}, got {t.dtype}")
+    return dev
+
+
+def _need(t, dtype, name: str, contiguous: bool = True, device: Optional[int] = None) -> int:
+    """t is a tensor of `dtype` (a dtype or a tuple of them) on the library's
+    device type (on device index `device` when given), contiguous unless told
+    not.  Returns its device index."""
+    try:
+        dev = t.get_device()
+        dt = t.dtype
+    except AttributeError:
+        raise ValueError(f"{name} must be a tensor") from None
+    if (dev >= 0) != (_DEVICE_TYPE == "cuda"):
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and dev != device:
+        raise ValueError(f"{name} is on device {dev}, the call's tensors on {device}")
+    if dt is not dtype and (not isinstance(dtype, tuple) or dt not in dtype):
+        want = " or ".join(map(str, dtype)) if isinstance(dtype, tuple) else str(dtype)
+        raise ValueError(f"{name} must be {want}, got {dt}")
     if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    return dev
 
 
 def _need_len(t: torch.Tensor, n: int, name: str) -> None:
@@ -212,29 +232,35 @@ def _need_len(t: torch.Tensor, n: int, name: str) -> None:
 
 
 def _row_stride(t: torch.Tensor, name: str) -> int:
-    if t.dim() != 2 or t.stride(1) != 1:
+    st = t.stride()
+    if len(st) != 2 or st[1] != 1:
         raise ValueError(f"{name} must be 2-D with unit column stride")
-    return t.stride(0)
+    return st[0]
 
 
 def _need_rows(t: torch.Tensor, rows: int, cols: int, name: str) -> int:
     """A 2-D row buffer with at least `rows` rows of exactly `cols` columns
     and unit column stride; returns its row stride."""
-    stride = _row_stride(t, name)
-    if t.shape[1] != cols:
-        raise ValueError(f"{name} rows hold {t.shape[1]} columns, the call needs {cols}")
-    if t.shape[0] < rows:
-        raise ValueError(f"{name} has {t.shape[0]} rows, the call needs {rows}")
-    return stride
+    st = t.stride()
+    if len(st) != 2 or st[1] != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    shape = t.shape
+    if shape[1] != cols:
+        raise ValueError(f"{name} rows hold {shape[1]} columns, the call needs {cols}")
+    if shape[0] < rows:
+        raise ValueError(f"{name} has {shape[0]} rows, the call needs {rows}")
+    return st[0]
 
 
-def _need_ids(expert_ids, name: str = "expert_ids", bs: Optional[int] = None, device=None):
+def _need_ids(expert_ids, name: str = "expert_ids", bs: Optional[int] = None,
+              device: Optional[int] = None):
     _need(expert_ids, torch.int32, name, device=device)
-    if expert_ids.dim() != 2:
+    shape = expert_ids.shape
+    if len(shape) != 2:
         raise ValueError(f"{name} must be [BS, K]")
-    if bs is not None and expert_ids.shape[0] != bs:
-        raise ValueError(f"{name} has {expert_ids.shape[0]} rows, x has {bs}")
-    return expert_ids.shape
+    if bs is not None and shape[0] != bs:
+        raise ValueError(f"{name} has {shape[0]} rows, x has {bs}")
+    return shape
 
 
 def _dtype_code(out_dtype: str) -> int:
@@ -244,6 +270,11 @@ def _dtype_code(out_dtype: str) -> int:
     return codes[out_dtype]
 
 
+def _new(shape, dtype, device: int):
+    return torch.empty(shape, dtype=dtype, device=torch.device(_DEVICE_TYPE, device)
+                       if device >= 0 else "cpu")
+
+
 class Layout(NamedTuple):
     expert_counts: torch.Tensor   # int32 [E]
     ep_send_counts: torch.Tensor  # int32 [E+1], exclusive padded prefix, last = M_pad
@@ -251,18 +282,19 @@ class Layout(NamedTuple):
     status: torch.Tensor          # int32 [1], moe_flag bits
 
 
-def _layout(out: Optional[Layout], n_experts: int, n_pairs: int, device) -> Layout:
+_LAYOUT_NAMES = ("out.expert_counts", "out.ep_send_counts", "out.expand_idx", "out.status")
+
+
+def _layout(out: Optional[Layout], n_experts: int, n_pairs: int, device: int) -> Layout:
     """The caller's Layout, checked against the call's sizes, or a new one."""
     if out is None:
-        return Layout(torch.empty(n_experts, dtype=torch.int32, device=device),
-                      torch.empty(n_experts + 1, dtype=torch.int32, device=device),
-                      torch.empty(n_pairs, dtype=torch.int32, device=device),
-                      torch.empty(1, dtype=torch.int32, device=device))
-    for t, n, name in ((out.expert_counts, n_experts, "expert_counts"),
-                       (out.ep_send_counts, n_experts + 1, "ep_send_counts"),
-                       (out.expand_idx, n_pairs, "expand_idx"), (out.status, 1, "status")):
-        _need(t, torch.int32, f"out.{name}", device=device)
-        _need_len(t, n, f"out.{name}")
+        return Layout(_new(n_experts, torch.int32, device),
+                      _new(n_experts + 1, torch.int32, device),
+                      _new(n_pairs, torch.int32, device), _new(1, torch.int32, device))
+    for t, n, name in zip(out, (n_experts, n_experts + 1, n_pairs, 1), _LAYOUT_NAMES):
+        _need(t, torch.int32, name, device=device)
+        if t.numel() < n:
+            raise ValueError(f"{name} holds {t.numel()} elements, the call needs {n}")
     return out
 
 
@@ -271,7 +303,7 @@ def _workspace(workspace: Optional[torch.Tensor], bs: int, k: int, n_experts: in
     None when the layout needs none."""
     ws_bytes = moe_dispatch_layout_workspace_size(bs, k, n_experts)
     if workspace is None:
-        return torch.zeros(ws_bytes, dtype=torch.uint8, device=device) if ws_bytes else None
+        return _new(ws_bytes, torch.uint8, device).zero_() if ws_bytes else None
     _need(workspace, workspace.dtype, "workspace", device=device)
     if _nbytes(workspace) < ws_bytes:
         raise ValueError(f"workspace holds {_nbytes(workspace)} bytes, the call needs {ws_bytes}")
@@ -289,31 +321,46 @@ def _scatter_outputs(expand_x, quant_scales, capacity_rows, bs, k, hidden, n_exp
         raise ValueError("capacity_rows must be >= 0")
     row_dtype = torch.bfloat16 if dtype == MOE_BF16 else torch.uint8
     if expand_x is None:
-        expand_x = torch.empty((capacity_rows, hidden), dtype=row_dtype, device=device)
+        expand_x = _new((capacity_rows, hidden), row_dtype, device)
     _need(expand_x, row_dtype, "expand_x", contiguous=False, device=device)
     _need_rows(expand_x, capacity_rows, hidden, "expand_x")
     if dtype == MOE_FP8_E4M3:
         if hidden % 128:
             raise ValueError("e4m3 output needs hidden to be a multiple of 128")
         if quant_scales is None:
-            quant_scales = torch.empty((capacity_rows, hidden // 128), dtype=torch.float32,
-                                       device=device)
+            quant_scales = _new((capacity_rows, hidden // 128), torch.float32, device)
         _need(quant_scales, torch.float32, "quant_scales", device=device)
         _need_rows(quant_scales, capacity_rows, hidden // 128, "quant_scales")
     return capacity_rows, expand_x, quant_scales
 
 
+# Size queries, memoised per library (their answers depend only on the
+# arguments): the checks ask for them on every call.
+_sizes: dict = {}
+
+
 def moe_dispatch_capacity(bs: int, k: int, num_experts: int, align: int = 128) -> int:
-    cap = load_library().moe_dispatch_capacity(bs, k, num_experts, align)
+    lib = load_library()
+    key = (id(lib), "cap", bs, k, num_experts, align)
+    cap = _sizes.get(key)
+    if cap is None:
+        cap = _sizes.setdefault(key, int(lib.moe_dispatch_capacity(bs, k, num_experts, align)))
     if cap < 0:
         raise MoeError(MOE_ERR_INVALID_ARG, "invalid layout arguments")
-    return int(cap)
+    return cap
 
 
 def moe_dispatch_layout_workspace_size(bs: int, k: int, num_experts: int) -> int:
     """Bytes of device workspace the layout needs (0: none).  A workspace must
-    be zero-filled before its first use; every call leaves it so."""
-    return int(load_library().moe_dispatch_layout_workspace_size(bs, k, num_experts))
+    be zero-filled before its first use; every call leaves its first word (an
+    arrival counter) zero, the only part that needs initial contents."""
+    lib = load_library()
+    key = (id(lib), "ws", bs, k, num_experts)
+    n = _sizes.get(key)
+    if n is None:
+        n = _sizes.setdefault(key, int(lib.moe_dispatch_layout_workspace_size(bs, k,
+                                                                             num_experts)))
+    return n
 
 
 def moe_dispatch_layout(expert_ids: torch.Tensor, num_experts: int, align: int = 128, *,
@@ -324,7 +371,7 @@ def moe_dispatch_layout(expert_ids: torch.Tensor, num_experts: int, align: int =
     With check=True the call waits for the GPU and raises MoeStatusError if
     the status word reports out-of-range or repeated ids."""
     bs, k = _need_ids(expert_ids)
-    dev = expert_ids.device
+    dev = expert_ids.get_device()
     out = _layout(out, num_experts, bs * k, dev)
     workspace = _workspace(workspace, bs, k, num_experts, dev)
     rc = load_library().moe_dispatch_layout(
@@ -347,11 +394,11 @@ def _routes(expert_ids, expand_idx, ep_send_counts, num_experts, bs, dev):
     return k
 
 
-def _status_word(status: Optional[torch.Tensor], check: bool, dev):
+def _status_word(status: Optional[torch.Tensor], check: bool, dev: int):
     """The in/out status word of a scatter or combine: the caller's (checked),
     or with check=True a new zeroed one."""
     if status is None:
-        return torch.zeros(1, dtype=torch.int32, device=dev) if check else None
+        return _new(1, torch.int32, dev).zero_() if check else None
     _need(status, torch.int32, "status", device=dev)
     _need_len(status, 1, "status")
     return status
@@ -369,8 +416,7 @@ def moe_dispatch(x: torch.Tensor, expert_ids: torch.Tensor, expand_idx: torch.Te
     moe_dispatch_capacity is allowed (a caller that knows the padded total
     may size the buffer to it); pairs past it are dropped and flagged
     MOE_FLAG_GUARD, which check=True turns into MoeStatusError."""
-    _need(x, torch.bfloat16, "x", contiguous=False)
-    dev = x.device
+    dev = _need(x, torch.bfloat16, "x", contiguous=False)
     if x.dim() != 2:
         raise ValueError("x must be [BS, H]")
     bs, hidden = x.shape
@@ -400,8 +446,7 @@ def moe_dispatch_fused(x: torch.Tensor, expert_ids: torch.Tensor, num_experts: i
     of at most 2048 pairs, two above).  Returns ``(layout, expand_x)`` or
     ``(layout, expand_x, quant_scales)``.  check=True waits for the GPU and
     raises MoeStatusError on any status bit."""
-    _need(x, torch.bfloat16, "x", contiguous=False)
-    dev = x.device
+    dev = _need(x, torch.bfloat16, "x", contiguous=False)
     if x.dim() != 2:
         raise ValueError("x must be [BS, H]")
     bs, hidden = x.shape
@@ -434,8 +479,7 @@ def moe_dispatch_fused_noalloc(x: torch.Tensor, expert_ids: torch.Tensor, num_ex
     `expand_x` and, for e4m3, `quant_scales` to allocate nothing at all).
     Batches whose workspace exceeds moe_noalloc_scratch_bytes() raise
     MoeError (MOE_ERR_SCRATCH).  Calls that overlap on one GPU race."""
-    _need(x, torch.bfloat16, "x", contiguous=False)
-    dev = x.device
+    dev = _need(x, torch.bfloat16, "x", contiguous=False)
     if x.dim() != 2:
         raise ValueError("x must be [BS, H]")
     bs, hidden = x.shape
@@ -468,7 +512,7 @@ def _combine_rows(shared_expert_x, out, bs, hidden, dev):
         if shared_expert_x.shape[0] != bs:
             raise ValueError(f"shared_expert_x has {shared_expert_x.shape[0]} rows, BS is {bs}")
     if out is None:
-        out = torch.empty((bs, hidden), dtype=torch.bfloat16, device=dev)
+        out = _new((bs, hidden), torch.bfloat16, dev)
     _need(out, torch.bfloat16, "out", device=dev)
     if tuple(out.shape) != (bs, hidden):
         raise ValueError(f"out must be [{bs}, {hidden}], got {list(out.shape)}")
@@ -483,8 +527,7 @@ def moe_combine(expand_x: torch.Tensor, expert_ids: torch.Tensor, expand_idx: to
     """x_out[t] = sum_j expert_scales[t,j] * expand_x[slot(t,j)] + shared_expert_x[t].
     check=True waits for the GPU and raises MoeStatusError if a slot fell
     outside expand_x (that pair contributed nothing)."""
-    _need(expand_x, torch.bfloat16, "expand_x", contiguous=False)
-    dev = expand_x.device
+    dev = _need(expand_x, torch.bfloat16, "expand_x", contiguous=False)
     bs, k = _need_ids(expert_ids, device=dev)
     _routes(expert_ids, expand_idx, ep_send_counts, num_experts, bs, dev)
     _need(expert_scales, torch.float32, "expert_scales", device=dev)
@@ -510,8 +553,7 @@ def moe_combine_fp8(expand_x: torch.Tensor, quant_scales: torch.Tensor, expert_i
                     status: Optional[torch.Tensor] = None, check: bool = False) -> torch.Tensor:
     """Combine over e4m3 expert rows (uint8 codes [cap, H]) with fp32 scales
     [cap, H/128], each term dequantised before the weighted sum."""
-    _need(expand_x, torch.uint8, "expand_x", contiguous=False)
-    dev = expand_x.device
+    dev = _need(expand_x, torch.uint8, "expand_x", contiguous=False)
     bs, k = _need_ids(expert_ids, device=dev)
     _routes(expert_ids, expand_idx, ep_send_counts, num_experts, bs, dev)
     _need(expert_scales, torch.float32, "expert_scales", device=dev)
@@ -544,7 +586,7 @@ def _replica_tables(replica_offsets, replica_thresholds, num_experts, dev):
 
 def _replica_ids(replica_ids, bs, k, dev):
     if replica_ids is None:
-        return torch.empty((bs, k), dtype=torch.int32, device=dev)
+        return _new((bs, k), torch.int32, dev)
     _need(replica_ids, torch.int32, "replica_ids", device=dev)
     _need_len(replica_ids, bs * k, "replica_ids")
     return replica_ids
@@ -561,7 +603,7 @@ def moe_dispatch_layout_replicated(expert_ids: torch.Tensor, num_experts: int,
     uint32 thresholds, given as int32 or uint32 bit patterns) and lay the
     pairs out over the replicas.  Returns ``(replica_ids [BS, K], Layout)``."""
     bs, k = _need_ids(expert_ids)
-    dev = expert_ids.device
+    dev = expert_ids.get_device()
     p = _replica_tables(replica_offsets, replica_thresholds, num_experts, dev)
     out = _layout(out, p, bs * k, dev)
     replica_ids = _replica_ids(replica_ids, bs, k, dev)
@@ -590,8 +632,7 @@ def moe_dispatch_fused_replicated(x: torch.Tensor, expert_ids: torch.Tensor, num
     """moe_dispatch_layout_replicated + moe_dispatch over the replicas in one
     call.  Returns ``(replica_ids, layout, expand_x)`` or ``(replica_ids,
     layout, expand_x, quant_scales)``."""
-    _need(x, torch.bfloat16, "x", contiguous=False)
-    dev = x.device
+    dev = _need(x, torch.bfloat16, "x", contiguous=False)
     if x.dim() != 2:
         raise ValueError("x must be [BS, H]")
     bs, hidden = x.shape
@@ -626,10 +667,10 @@ def moe_dispatch_layout_ep(expert_ids: torch.Tensor, num_experts: int, ep_world_
     and contiguously over ``ep_world_size`` ranks).  Returns
     ``(Layout, rank_offsets int32 [ws+1])``."""
     bs, k = _need_ids(expert_ids)
-    dev = expert_ids.device
+    dev = expert_ids.get_device()
     out = _layout(out, num_experts, bs * k, dev)
     if rank_offsets is None:
-        rank_offsets = torch.empty(max(ep_world_size, 0) + 1, dtype=torch.int32, device=dev)
+        rank_offsets = _new(max(ep_world_size, 0) + 1, torch.int32, dev)
     _need(rank_offsets, torch.int32, "rank_offsets", device=dev)
     _need_len(rank_offsets, max(ep_world_size, 0) + 1, "rank_offsets")
     workspace = _workspace(workspace, bs, k, num_experts, dev)
