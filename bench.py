@@ -86,6 +86,13 @@ def parse():
                         "dispatch's and combine's read:write mixes)")
     p.add_argument("--copy-probe", action="store_true",
                    help="run only a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--latency-floor", action="store_true",
+                   help="print only per-launch times, in 10-launch HIP graphs, of an empty "
+                        "kernel, the plain gather and scatter probes at the workload's layout "
+                        "rows, and the path's own kernels (decode-sized latency floor)")
+    p.add_argument("--layout-sweep", action="store_true",
+                   help="print only moe_dispatch_layout kernel times at 32K to 64M pairs "
+                        "(E = 256, K = 8), each launch timed by bound events")
     return p.parse_args()
 
 
@@ -231,6 +238,104 @@ def buffer_sets(w, cap, step_bytes, fp8_combine):
     return max(1, min(max(by_cache, by_volume), SET_MEMORY_CAP // per_set, 64))
 
 
+def per_launch_in_graphs(fn, launches=10, replays=30):
+    """Median microseconds per launch of `fn` captured `launches` times in one
+    HIP graph, each replay bracketed by events on the stream (the graph's
+    launch gap included, as in a serving loop that replays a whole pass)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(launches):
+            fn()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(replays)]
+    for a, z in evs:
+        a.record()
+        g.replay()
+        z.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(z) for a, z in evs)
+    return round(t[len(t) // 2] * 1e3 / launches, 2)
+
+
+def latency_floor(moe, w, b, ids, scales, n_phys, cap, front, combine):
+    """The decode-sized step against the latency floor of its launches: an
+    empty kernel (one workgroup, and the combine's grid), the plain gather
+    probe with the combine's reads at this routing's layout rows (K expert
+    rows + the shared row per token, one row written: one dependent load of
+    the row indices, then the rows), the scatter probe with the dispatch's
+    writes at the same rows, and the path's own kernels, all in 10-launch
+    graphs on one buffer set."""
+    import torch
+    lay = front(b)
+    torch.cuda.synchronize()
+    slots = (lay.ep_send_counts[ids.reshape(-1).long()].long()
+             + lay.expand_idx.long()).view(w.bs, w.topk).to(torch.int32)
+    cols = w.hidden // 2                          # int32 columns of a bf16 row
+    grid_combine = w.bs * (-(-(w.hidden // 8) // 128))
+    y_rows = torch.zeros((cap + w.bs, cols), dtype=torch.int32, device="cuda")
+    out_rows = torch.empty((max(cap, w.bs), cols), dtype=torch.int32, device="cuda")
+    shared_rows = (cap + torch.arange(w.bs, dtype=torch.int32, device="cuda"))[:, None]
+    gather_src = torch.cat([slots, shared_rows], dim=1).reshape(-1).contiguous()
+    scatter_dst = slots.reshape(-1).contiguous()
+    x_rows = torch.zeros((w.bs, cols), dtype=torch.int32, device="cuda")
+    res = {
+        "empty_kernel_1_workgroup": per_launch_in_graphs(lambda: moe.moe_probe_empty(1)),
+        f"empty_kernel_{grid_combine}_workgroups": per_launch_in_graphs(
+            lambda: moe.moe_probe_empty(grid_combine)),
+        "gather_probe_combine_reads": per_launch_in_graphs(
+            lambda: moe.moe_probe_stream_mix(y_rows, out_rows, w.bs, w.topk + 1, 1,
+                                             gather_src, None)),
+        "scatter_probe_dispatch_writes": per_launch_in_graphs(
+            lambda: moe.moe_probe_stream_mix(x_rows, out_rows, w.bs, 1, w.topk, None,
+                                             scatter_dst)),
+        "layout+dispatch": per_launch_in_graphs(lambda: front(b)),
+        "combine": per_launch_in_graphs(lambda: combine(b, lay)),
+        "step": per_launch_in_graphs(lambda: combine(b, front(b))),
+    }
+    return res
+
+
+def layout_sweep(moe):
+    """moe_dispatch_layout kernel time (all of its launches, each timed by
+    events bound to it; median of 20 calls) at growing pair counts, E = 256,
+    K = 8, routing (h_t + j) mod E with a seeded uniform h_t."""
+    import numpy as np
+    import torch
+    out = {}
+    for pairs in (1 << 15, 1 << 20, 1 << 22, 1 << 24, 1 << 26):
+        bs, k, e = pairs // 8, 8, 256
+        h = torch.from_numpy(np.random.default_rng(pairs).integers(0, e, bs, dtype=np.int32))
+        ids = ((h[:, None] + torch.arange(k, dtype=torch.int32)) % e).to(torch.int32).cuda()
+        lay = moe.moe_dispatch_layout(ids, e, 128)
+        ws = torch.zeros(max(moe.moe_dispatch_layout_workspace_size(bs, k, e), 16),
+                         dtype=torch.uint8, device="cuda")
+        times = []
+        for _ in range(23):
+            pairs_ev = [(torch.cuda.Event(enable_timing=True),
+                         torch.cuda.Event(enable_timing=True)) for _ in range(2)]
+            for a, z in pairs_ev:
+                a.record()
+                z.record()
+            moe.moe_time_next_launches(pairs_ev)
+            moe.moe_dispatch_layout(ids, e, 128, out=lay, workspace=ws)
+            used = 2 - moe.moe_time_unused_launches()
+            moe.moe_time_next_launches([])
+            torch.cuda.synchronize()
+            times.append(sum(a.elapsed_time(z) for a, z in pairs_ev[:used]) * 1e3)
+        times = sorted(times[3:])
+        out[str(pairs)] = {"us": round(times[len(times) // 2], 2),
+                           "ns_per_1k_pairs": round(times[len(times) // 2] * 1e3 / (pairs / 1e3),
+                                                    3),
+                           "launches": used}
+        del ids, lay, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def practical_ceiling(moe, w, slots, cap, launches=16):
     """GB/s of the plain streaming probe with the dispatch's 1 : K and the
     combine's (K + 1) : 1 row mixes at this workload's bf16 row size and
@@ -315,6 +420,11 @@ def main():
     import workloads
 
     moe.load_library()
+    if args.layout_sweep:
+        torch.cuda.set_device(0)
+        print(json.dumps({"layout_sweep": layout_sweep(moe),
+                          "unit": "us per moe_dispatch_layout call (kernel time)"}), flush=True)
+        return
     w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -457,6 +567,11 @@ def main():
             return {"layout+dispatch (fused)": ms[0], "combine": ms[1]}
         return {"layout": sum(ms[:-2]), "dispatch": ms[-2], "combine": ms[-1],
                 "layout_launches": len(ms) - 2}
+
+    if args.latency_floor:
+        print(json.dumps({"workload": w.name, "latency_floor_us_per_launch": latency_floor(
+            moe, w, bufs[0], route_ids, scales, n_phys, cap, front, combine)}), flush=True)
+        return
 
     # Warm-up: at least one step per buffer set, so that every set has run
     # once before the timed region; the steps run are reported as

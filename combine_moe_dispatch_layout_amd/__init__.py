@@ -61,7 +61,7 @@ __all__ = [
     "moe_dispatch", "moe_dispatch_fused", "moe_dispatch_fused_replicated", "moe_combine",
     "moe_dispatch_fused_noalloc", "moe_noalloc_scratch_bytes",
     "moe_plan_compensation",
-    "moe_combine_fp8", "moe_probe_stream_mix", "moe_time_next_launches",
+    "moe_combine_fp8", "moe_probe_stream_mix", "moe_probe_empty", "moe_time_next_launches",
     "moe_time_unused_launches",
     "MOE_BF16", "MOE_FP8_E4M3", "MOE_FLAG_ID_RANGE", "MOE_FLAG_DUP_ID", "MOE_FLAG_GUARD",
 ]
@@ -120,6 +120,7 @@ def load_library() -> ctypes.CDLL:
         "moe_dispatch_layout_ep": (ctypes.c_int, [P, i32, i32, i32, i32, i32, P, P, P, P, P, P,
                                                   sz, P]),
         "moe_probe_stream_mix": (ctypes.c_int, [P, i64, P, i64, i32, i32, i32, i32, P, P, P]),
+        "moe_probe_empty": (ctypes.c_int, [i32, P]),
         "moe_time_next_launches": (ctypes.c_int, [P, P, i32]),
         "moe_time_unused_launches": (i32, []),
         "moe_dispatch_layout_replicated": (ctypes.c_int, [P, i32, i32, i32, P, P, i32,
@@ -726,6 +727,16 @@ def moe_probe_stream_mix(src: torch.Tensor, dst: torch.Tensor, items: int, reads
         _ptr(src), src.shape[0], _ptr(dst), dst.shape[0], items, row_bytes, reads, writes,
         _ptr(src_rows), _ptr(dst_rows), _stream(src))
     _check(rc)
+
+
+def moe_probe_empty(workgroups: int, device: Optional[int] = None) -> None:
+    """Measurement probe (include/moe_probe.h): an empty kernel of
+    `workgroups` workgroups on the current stream of `device` (the current
+    device when None), the latency floor of one launch of that grid."""
+    dev = torch.cuda.current_device() if device is None else device
+    stream = _raw_stream(dev) if _raw_stream is not None else \
+        torch.cuda.current_stream(dev).cuda_stream
+    _check(load_library().moe_probe_empty(workgroups, stream))
 
 
 def moe_time_next_launches(pairs) -> None:

@@ -40,7 +40,7 @@ def _obj_dir() -> str:
     return d
 
 
-# Build-time tuning macros (for example "-DMOE_FUSED_DEFER=0"); the
+# Build-time tuning macros (for example "-DMOE_CACHED_ROWS_PER_CU=8"); the
 # defaults in csrc/moe_internal.h are the measured choices.
 EXTRA = os.environ.get("MOE_HIPCC_DEFINES", "").split()
 

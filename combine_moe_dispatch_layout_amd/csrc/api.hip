@@ -106,10 +106,11 @@ int layout_then_scatter(const void* x, int64_t x_stride, int32_t bs, int32_t hid
     const int64_t max_vecs = moe::kReadAheadMaxBytes / 16;
     ahead.base = static_cast<const moe::u32x4*>(x);
     ahead.vecs = vecs < max_vecs ? vecs : max_vecs;
-    ahead.split = ahead.vecs * moe::kReadAheadRankPercent / 100;
     rows_cached = ahead.vecs == vecs && moe::read_ahead_runs(plan, ahead);
   }
-  const bool defer = moe::kFusedDefer && plan.blocks > 1;
+  // With several ranking workgroups the ranks are left to the scatter (no
+  // finalize launch).
+  const bool defer = plan.blocks > 1;
   hipError_t err = moe::launch_layout(expert_ids, k, ranked, align, plan, counts, send,
                                       expand_idx, status, workspace, map, moe::RankSplit{}, s,
                                       ahead, defer);

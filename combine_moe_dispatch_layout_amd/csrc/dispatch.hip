@@ -5,7 +5,9 @@
 //
 // Work split: one workgroup per item = (token, chunk of the row).  The
 // workgroup stages ep_send_counts in LDS while lanes 0..K-1 fetch the token's
-// ids and ranks, so the routes cost one memory round trip plus one LDS read.
+// ids and ranks, so the routes cost one memory round trip plus one LDS read
+// (in large grids of rows from HBM the staging is deliberately slower; see
+// Staging below).
 // A row chunk is read once with 16-byte loads and written K times with
 // 16-byte non-temporal stores (the dispatched rows are write-once streams).
 // Every destination row is checked against capacity_rows before any store.
@@ -39,7 +41,34 @@ struct RouteTables {
     __syncthreads();
     return DEFER ? lds + kBase : nullptr;
   }
+  // The same tables, each thread staging its entries one load at a time
+  // (a round trip per entry; see Staging::kRowsFirstSerial).
+  __device__ __forceinline__ static const int* stage_serial(
+      int* lds, const int32_t* __restrict__ send_counts, const DeferredRanks& dr, int32_t t,
+      int32_t E) {
+    if (DEFER) {
+      const int32_t* row = dr.base + (int64_t)(t / dr.tokens_per_block) * E;
+      for (int e = threadIdx.x; e < E; e += THREADS) lds[kBase + e] = row[e];
+    }
+    for (int e = threadIdx.x; e <= E; e += THREADS) lds[e] = send_counts[e];
+    __syncthreads();
+    return DEFER ? lds + kBase : nullptr;
+  }
 };
+
+// Order of a workgroup's loads before its stores, chosen per launch:
+//  - kTablesFirst: the tables' loads, then the row's (rows already in the
+//    Infinity Cache); staging is one round trip and the routes need not wait
+//    for the row;
+//  - kRowsFirst: the row's loads (from HBM), then the tables' in one round
+//    trip that overlaps the row's latency (latency-bound, decode-sized
+//    grids);
+//  - kRowsFirstSerial: the row's loads, then the tables staged one load at a
+//    time per thread.  The longer workgroup life leaves fewer writes in
+//    flight, which HBM takes faster in bandwidth-bound grids (measured on the
+//    16384-token, E = 512 line: 374 us against 401 us batched, with the cap
+//    of kUncachedPerCu workgroups per compute unit).
+enum class Staging { kTablesFirst, kRowsFirst, kRowsFirstSerial };
 
 // With deferred ranks, the first-chunk workgroup of token t writes the
 // token's final expand_idx (rank within the workgroup + column prefix).
@@ -54,7 +83,7 @@ __device__ __forceinline__ void write_deferred(const PairMeta& m, const int* bas
 
 // LDS_INTS sizes the offset tables; a larger array than they need only
 // serves to cap how many workgroups share a compute unit.
-template <int THREADS, int VPT, int KMAX, int LDS_INTS, bool DEFER>
+template <int THREADS, int VPT, int KMAX, int LDS_INTS, bool DEFER, Staging ORDER>
 __global__ __launch_bounds__(THREADS) void dispatch_bf16_kernel(
     const u32x4* x, int64_t xs, int32_t nvec, int32_t nchunks,
     const int32_t* __restrict__ ids, const int32_t* __restrict__ idx,
@@ -66,18 +95,30 @@ __global__ __launch_bounds__(THREADS) void dispatch_bf16_kernel(
   const int32_t chunk = blockIdx.x - t * nchunks;
   PairMeta meta;
   fetch_pair_meta(meta, t, k, ids, idx, nullptr);
-  RouteTables<THREADS, DEFER> tables;
-  tables.load(send, dr, t, E);
-  // The row loads go out after the tables' loads, so the routes need not
-  // wait for them.
-  // (A lane past the row end repeats the last vector and stores nothing.)
+  // (A lane past the row end repeats the last vector and stores nothing, so
+  // the row loads need no branch.)
   const int32_t v0 = chunk * (THREADS * VPT) + threadIdx.x;
   const u32x4* src = x + (int64_t)t * xs;
   u32x4 r[VPT];
+  RouteTables<THREADS, DEFER> tables;
+  const int* base_lds;
+  if (ORDER == Staging::kRowsFirstSerial) {
 #pragma unroll
-  for (int j = 0; j < VPT; ++j) r[j] = src[min(v0 + j * THREADS, nvec - 1)];
-  keep_order();
-  const int* base_lds = tables.store(lds);
+    for (int j = 0; j < VPT; ++j) r[j] = src[min(v0 + j * THREADS, nvec - 1)];
+    base_lds = RouteTables<THREADS, DEFER>::stage_serial(lds, send, dr, t, E);
+  } else {
+    if (ORDER == Staging::kRowsFirst) {
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) r[j] = src[min(v0 + j * THREADS, nvec - 1)];
+      tables.load(send, dr, t, E);
+    } else {
+      tables.load(send, dr, t, E);
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) r[j] = src[min(v0 + j * THREADS, nvec - 1)];
+    }
+    keep_order();
+    base_lds = tables.store(lds);
+  }
   int64_t slot[KMAX];
   float unused_w[KMAX];
   resolve_routes<KMAX>(meta, lds, base_lds, k, E, cap, slot, unused_w, status,
@@ -150,15 +191,18 @@ __global__ __launch_bounds__(THREADS) void dispatch_fp8_kernel(
 
 int kmax_for(int32_t k) { return k <= 2 ? 2 : k <= 4 ? 4 : k <= 8 ? 8 : 16; }
 
-// Launch shape of the bf16 scatter.  With the token rows already in the
-// Infinity Cache (read ahead by the layout's ranking launch), the scatter is
-// bound by its row writes alone, and HBM takes them faster from fewer waves
-// in flight, which write a narrower window of destination rows: 64-thread
-// workgroups holding enough LDS that at most 7 share a compute unit (under 2
-// waves per SIMD).  Rows that still come from HBM need the latency
-// hiding of full occupancy, so they keep 128-thread workgroups with only
-// the send counts in LDS.
-template <int THREADS, int LDS_INTS, bool DEFER>
+// Launch shapes of the bf16 scatter.
+//  - Token rows already in the Infinity Cache (read ahead by the layout's
+//    ranking launch): the scatter is bound by its row writes alone, and HBM
+//    takes them faster from fewer waves in flight, which write a narrower
+//    window of destination rows: 64-thread workgroups holding enough LDS
+//    that at most kCachedRowsPerCu share a compute unit.
+//  - Rows from HBM: 128-thread workgroups.  Grids of at least
+//    kSerialMinItems workgroups (bandwidth bound) stage their tables one load
+//    at a time per thread and are capped at kUncachedPerCu workgroups per
+//    compute unit; smaller, latency-bound grids stage in one round trip at
+//    full occupancy.
+template <int THREADS, int LDS_INTS, bool DEFER, Staging ORDER>
 hipError_t launch_bf16_shape(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
                              const int32_t* ids, const int32_t* expand_idx, const int32_t* send,
                              int32_t k, int32_t num_experts, void* expand_x,
@@ -172,28 +216,17 @@ hipError_t launch_bf16_shape(const void* x, int64_t x_stride, int32_t bs, int32_
   const u32x4* xv = static_cast<const u32x4*>(x);
   u32x4* ov = static_cast<u32x4*>(expand_x);
   const int64_t xs = x_stride / 8, os = expand_x_stride / 8;
+#define MOE_SCATTER(KM)                                                                     \
+  launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, KM, LDS_INTS, DEFER, ORDER>, grid,      \
+      THREADS, stream, xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os, \
+      capacity_rows, status, dr)
   switch (kmax_for(k)) {
-    case 2:
-      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 2, LDS_INTS, DEFER>, grid, THREADS,
-          stream, xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          capacity_rows, status, dr);
-      break;
-    case 4:
-      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 4, LDS_INTS, DEFER>, grid, THREADS,
-          stream, xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          capacity_rows, status, dr);
-      break;
-    case 8:
-      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 8, LDS_INTS, DEFER>, grid, THREADS,
-          stream, xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          capacity_rows, status, dr);
-      break;
-    default:
-      launch_kernel(dispatch_bf16_kernel<THREADS, kVpt, 16, LDS_INTS, DEFER>, grid, THREADS,
-          stream, xv, xs, nvec, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          capacity_rows, status, dr);
-      break;
+    case 2: MOE_SCATTER(2); break;
+    case 4: MOE_SCATTER(4); break;
+    case 8: MOE_SCATTER(8); break;
+    default: MOE_SCATTER(16); break;
   }
+#undef MOE_SCATTER
   return hipGetLastError();
 }
 
@@ -237,14 +270,22 @@ hipError_t launch_fp8_shape(const void* x, int64_t x_stride, int32_t bs, int32_t
   return hipGetLastError();
 }
 
+// LDS ints per workgroup such that `per_cu` workgroups fit a compute
+// unit's 160 KB and one more does not (in 512-byte steps).
+constexpr int lds_ints_for(int per_cu) { return (163840 / per_cu) / 512 * 512 / 4; }
+
 #ifndef MOE_CACHED_ROWS_PER_CU
 #define MOE_CACHED_ROWS_PER_CU 7   // workgroups of the cache-resident scatter per compute unit
 #endif
 constexpr int kCachedRowsThreads = 64;
-// LDS per workgroup such that MOE_CACHED_ROWS_PER_CU fit a compute unit's
-// 160 KB and one more does not (in 512-byte steps).
-constexpr int kCachedRowsLdsInts = (163840 / MOE_CACHED_ROWS_PER_CU) / 512 * 512 / 4;
-static_assert((MOE_CACHED_ROWS_PER_CU + 1) * kCachedRowsLdsInts * 4 > 163840, "cap");
+constexpr int kCachedRowsPerCu = MOE_CACHED_ROWS_PER_CU;
+constexpr int kCachedRowsLdsInts = lds_ints_for(kCachedRowsPerCu);
+static_assert((kCachedRowsPerCu + 1) * kCachedRowsLdsInts * 4 > 163840, "cap");
+#ifndef MOE_UNCACHED_PER_CU
+#define MOE_UNCACHED_PER_CU 12     // large HBM-bound grids: workgroups per compute unit
+#endif
+constexpr int kUncachedPerCu = MOE_UNCACHED_PER_CU;
+constexpr int kUncachedLdsInts = lds_ints_for(kUncachedPerCu);
 
 }  // namespace
 
@@ -254,21 +295,27 @@ hipError_t launch_dispatch_bf16(const void* x, int64_t x_stride, int32_t bs, int
                                 void* expand_x, int64_t expand_x_stride, int64_t capacity_rows,
                                 int32_t* status, hipStream_t stream, bool rows_cached,
                                 const DeferredRanks& dr) {
-  if (rows_cached && dr.base)
-    return launch_bf16_shape<kCachedRowsThreads, kCachedRowsLdsInts, true>(
-        x, x_stride, bs, hidden, ids, expand_idx, send, k, num_experts, expand_x,
-        expand_x_stride, capacity_rows, status, stream, dr);
-  if (rows_cached)
-    return launch_bf16_shape<kCachedRowsThreads, kCachedRowsLdsInts, false>(
-        x, x_stride, bs, hidden, ids, expand_idx, send, k, num_experts, expand_x,
-        expand_x_stride, capacity_rows, status, stream, dr);
-  if (dr.base)
-    return launch_bf16_shape<MOE_DISPATCH_THREADS, RouteTables<MOE_DISPATCH_THREADS, true>::kInts, true>(
-        x, x_stride, bs, hidden, ids, expand_idx, send, k, num_experts, expand_x,
-        expand_x_stride, capacity_rows, status, stream, dr);
-  return launch_bf16_shape<MOE_DISPATCH_THREADS, RouteTables<MOE_DISPATCH_THREADS, false>::kInts, false>(
-      x, x_stride, bs, hidden, ids, expand_idx, send, k, num_experts, expand_x,
-      expand_x_stride, capacity_rows, status, stream, dr);
+  constexpr int kT = MOE_DISPATCH_THREADS;
+  const int64_t items = (int64_t)bs * ((hidden / 8 + kT - 1) / kT);
+  const bool big = items >= kSerialMinItems;
+#define MOE_SHAPE(TH, LDS, DEF, ORD)                                                      \
+  return launch_bf16_shape<TH, LDS, DEF, ORD>(x, x_stride, bs, hidden, ids, expand_idx,   \
+      send, k, num_experts, expand_x, expand_x_stride, capacity_rows, status, stream, dr)
+  if (rows_cached) {
+    if (dr.base) MOE_SHAPE(kCachedRowsThreads, kCachedRowsLdsInts, true, Staging::kTablesFirst);
+    MOE_SHAPE(kCachedRowsThreads, kCachedRowsLdsInts, false, Staging::kTablesFirst);
+  }
+  constexpr int kLdsD = RouteTables<kT, true>::kInts;
+  constexpr int kLdsN = RouteTables<kT, false>::kInts;
+  constexpr int kCapD = kUncachedLdsInts > kLdsD ? kUncachedLdsInts : kLdsD;
+  constexpr int kCapN = kUncachedLdsInts > kLdsN ? kUncachedLdsInts : kLdsN;
+  if (big) {
+    if (dr.base) MOE_SHAPE(kT, kCapD, true, Staging::kRowsFirstSerial);
+    MOE_SHAPE(kT, kCapN, false, Staging::kRowsFirstSerial);
+  }
+  if (dr.base) MOE_SHAPE(kT, kLdsD, true, Staging::kRowsFirst);
+  MOE_SHAPE(kT, kLdsN, false, Staging::kRowsFirst);
+#undef MOE_SHAPE
 }
 
 hipError_t launch_dispatch_fp8(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     ReplicaMap map, RankSplit ranks, ReadAhead ahead, int32_t rank_blocks,
     int32_t ahead_blocks) {
   if ((int32_t)blockIdx.x >= rank_blocks) {
-    read_ahead(ahead, rank_blocks, ahead_blocks, 0, ahead.split);
+    read_ahead(ahead, rank_blocks, ahead_blocks, 0, ahead.vecs);
     return;
   }
   __shared__ unsigned long long mask[kLayoutWaves][kMaxExperts];  // 32 KB
@@ -364,15 +364,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
 
 // Adds each workgroup's column prefix (from the arrival-ordered scan) to the
 // ranks within that workgroup.  One workgroup per ranking workgroup.
-// Workgroups past nblocks read token rows ahead instead.
 __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
     const int32_t* __restrict__ ids, int32_t n_pairs, int32_t E, int64_t pairs_per_block,
-    const int32_t* __restrict__ base, int32_t* __restrict__ expand_idx, int32_t nblocks,
-    ReadAhead ahead, int32_t ahead_blocks) {
-  if ((int32_t)blockIdx.x >= nblocks) {
-    read_ahead(ahead, nblocks, ahead_blocks, ahead.split, ahead.vecs);
-    return;
-  }
+    const int32_t* __restrict__ base, int32_t* __restrict__ expand_idx) {
   __shared__ int base_lds[kMaxExperts];
   constexpr int kUnroll = 4;
   const int tid = threadIdx.x;
@@ -478,30 +472,25 @@ hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int
                          const ReadAhead& ahead, bool defer_ranks) {
   const int32_t ahead_blocks =
       read_ahead_runs(plan, ahead) ? kReadAheadMaxBlocks - plan.blocks : 0;
-  const bool finalize = plan.blocks > 1 && !defer_ranks;
-  // Without a finalize launch the ranking launch reads every row ahead.
-  ReadAhead ahead_used = ahead;
-  if (!finalize || ahead_blocks == 0) ahead_used.split = ahead.vecs;
   const LayoutScratch ws = layout_scratch(plan, num_experts, workspace);
   // With several workgroups and a scatter to follow, the ranks within the
   // workgroups stay in the workspace and the scatter completes expand_idx.
   int32_t* ranks_out = (plan.blocks > 1 && defer_ranks) ? ws.ranks : expand_idx;
   switch (plan.rounds) {
     case 1: launch_rank<1>(plan, ids, k, num_experts, align, ranks_out, ws, counts, send,
-                           status, map, ranks, stream, ahead_used, ahead_blocks); break;
+                           status, map, ranks, stream, ahead, ahead_blocks); break;
     case 2: launch_rank<2>(plan, ids, k, num_experts, align, ranks_out, ws, counts, send,
-                           status, map, ranks, stream, ahead_used, ahead_blocks); break;
+                           status, map, ranks, stream, ahead, ahead_blocks); break;
     default: launch_rank<4>(plan, ids, k, num_experts, align, ranks_out, ws, counts, send,
-                            status, map, ranks, stream, ahead_used, ahead_blocks); break;
+                            status, map, ranks, stream, ahead, ahead_blocks); break;
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.blocks <= 1 || defer_ranks) return err;
   // The finalize pass looks pairs up by the id they were ranked under.
   const int32_t* ranked_ids = map.offsets != nullptr ? map.out : ids;
-  const int32_t finalize_ahead = ahead_used.split < ahead_used.vecs ? ahead_blocks : 0;
-  launch_kernel(layout_finalize_kernel, plan.blocks + finalize_ahead, kLayoutThreads, stream,
-      ranked_ids, (int32_t)plan.n_pairs, num_experts, plan.pairs_per_block,
-      (const int32_t*)ws.hist, expand_idx, plan.blocks, ahead_used, finalize_ahead);
+  launch_kernel(layout_finalize_kernel, plan.blocks, kLayoutThreads, stream, ranked_ids,
+      (int32_t)plan.n_pairs, num_experts, plan.pairs_per_block, (const int32_t*)ws.hist,
+      expand_idx);
   return hipGetLastError();
 }
 

@@ -291,25 +291,16 @@ struct RankSplit {
 struct ReadAhead {
   const u32x4* base = nullptr;
   int64_t vecs = 0;   // 16-byte vectors, from base
-  int64_t split = 0;  // with a finalize launch: the ranking launch reads [0, split)
 };
-// Whether moe_dispatch_fused leaves the ranks within the ranking workgroups
-// to the scatter (two launches) or completes them in a finalize launch first
-// (three launches, the read-ahead split between the ranking and finalize
-// launches at MOE_READ_AHEAD_RANK_PERCENT).
-#ifndef MOE_FUSED_DEFER
-#define MOE_FUSED_DEFER 1
-#endif
-#ifndef MOE_READ_AHEAD_RANK_PERCENT
-#define MOE_READ_AHEAD_RANK_PERCENT 60
-#endif
-constexpr bool kFusedDefer = MOE_FUSED_DEFER != 0;
+// Streaming grids of at least this many workgroups (about two full waves of
+// workgroups on 256 compute units) are bandwidth bound; smaller ones are
+// latency bound.  The scatter of rows from HBM picks its staging by it.
+constexpr int64_t kSerialMinItems = 8192;
 // Static scratch of moe_dispatch_fused_noalloc, per GPU: enough for the
 // layout workspace of any batch of at most 2^20 pairs (E <= 512).
 #ifndef MOE_NOALLOC_SCRATCH_BYTES
 #define MOE_NOALLOC_SCRATCH_BYTES (size_t(5) << 20)
 #endif
-constexpr int kReadAheadRankPercent = MOE_READ_AHEAD_RANK_PERCENT;
 #ifndef MOE_READ_AHEAD_BLOCKS
 #define MOE_READ_AHEAD_BLOCKS 240  // of the 256 compute units, with the ranking workgroups
 #endif

@@ -75,8 +75,20 @@ __global__ __launch_bounds__(kProbeThreads) void stream_mix_kernel(
     if (w < W && wrow[w] >= 0 && wrow[w] < dst_total) store_stream(acc, dst + wrow[w] * nvec + v);
 }
 
+// Does nothing: the fixed cost of a launch (dispatch of the workgroups, the
+// end-of-kernel release) with no memory traffic, the latency floor of a
+// kernel of that grid.
+__global__ __launch_bounds__(kProbeThreads) void empty_kernel() {}
+
 }  // namespace
 }  // namespace moe
+
+extern "C" int moe_probe_empty(int32_t workgroups, void* stream) {
+  if (workgroups < 1) return MOE_ERR_INVALID_ARG;
+  moe::launch_kernel(moe::empty_kernel, dim3((uint32_t)workgroups), moe::kProbeThreads,
+                     static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
 
 extern "C" int moe_probe_stream_mix(const void* src, int64_t src_rows_total, void* dst,
                                     int64_t dst_rows_total, int32_t items, int32_t row_bytes,

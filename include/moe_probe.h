@@ -61,8 +61,8 @@ int moe_probe_stream_mix(const void* src, int64_t src_rows_total, void* dst,
  *
  * An entry point makes one launch per kernel: moe_dispatch_layout one or two
  * (one when a single workgroup ranks the batch), then moe_dispatch one;
- * moe_dispatch_fused one (fused kernel) or the layout's launches then the
- * dispatch's; moe_combine and moe_combine_fp8 one.  Calls that return an
+ * moe_dispatch_fused one (fused kernel, bs*k <= 2048) or two (the layout's
+ * ranking launch, then the scatter); moe_combine and moe_combine_fp8 one.  Calls that return an
  * error or have nothing to do launch nothing and leave the pairs bound.
  *
  *  n   in  0..16; a new call replaces the pairs still bound, and n = 0 only
@@ -77,6 +77,17 @@ int moe_time_next_launches(void* const* start_events, void* const* stop_events, 
 /* Number of pairs bound by moe_time_next_launches that no launch has taken
  * yet, on the calling host thread. */
 int32_t moe_time_unused_launches(void);
+
+/*
+ * An empty kernel of `workgroups` workgroups of 128 threads: the fixed cost
+ * of one launch of that grid (workgroup dispatch and the end-of-kernel
+ * release, no memory traffic), the latency floor against which the
+ * decode-sized kernels are read.
+ *  workgroups  in  >= 1.
+ * Returns MOE_ERR_INVALID_ARG (1) for workgroups < 1, MOE_ERR_HIP (4) if the
+ * launch fails, else 0.
+ */
+int moe_probe_empty(int32_t workgroups, void* stream);
 
 #ifdef __cplusplus
 }
