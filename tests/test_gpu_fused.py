@@ -6,8 +6,8 @@ the whole dispatched buffer bit-exact, including padding rows the call must
 leave untouched (pre-filled with the oracle's sentinel) and canary rows past
 capacity.  Batches of at most 2048 pairs take the one-launch kernels (bf16 and e4m3;
 e4m3 codes and scales bit-exact against the oracle's quantiser); larger
-batches take the layout + dispatch launches and must equal the separate
-calls.
+batches take the layout + dispatch launches and, like the separate calls,
+must give the oracle's whole buffer.
 """
 
 import numpy as np
@@ -104,28 +104,56 @@ def test_one_launch_guard_skips_rows_beyond_capacity():
 
 
 def test_two_launch_paths_equal_the_separate_calls():
+    """The separate layout + dispatch calls and moe_dispatch_fused, bf16 and
+    e4m3, into sentinel-filled buffers: both give the oracle's layout and
+    the oracle's whole dispatched buffer (e4m3 codes and scales of every
+    row, padding rows untouched)."""
     import combine_moe_dispatch_layout_amd as moe
     rng = np.random.default_rng(7)
     for bs, h, e, k, dtype in [(4097, 256, 64, 1, "bf16"), (700, 512, 64, 8, "bf16"),
                                (100, 1024, 32, 4, "fp8"), (600, 256, 16, 8, "fp8"),
-                               (128, 7168, 256, 8, "fp8")]:
-        ids = torch.from_numpy(random_ids(rng, bs, e, k)).to(DEV)
-        x = to_dev_bf16(random_bf16(rng, (bs, h)))
+                               (128, 7168, 256, 8, "fp8"), (1500, 7168, 256, 8, "fp8")]:
+        ids_h = random_ids(rng, bs, e, k)
+        x_bits = random_bf16(rng, (bs, h))
+        ids = torch.from_numpy(ids_h).to(DEV)
+        x = to_dev_bf16(x_bits)
         cap = moe.moe_dispatch_capacity(bs, k, e, 128)
+        c, s, r, f = oracle.layout(ids_h, e, 128)
+        assert f == 0
+
+        def buffers():
+            if dtype == "bf16":
+                return (torch.full((cap, h), oracle.SENTINEL_BF16, dtype=torch.int16,
+                                   device=DEV).view(torch.bfloat16), None)
+            return (torch.full((cap, h), oracle.SENTINEL_FP8, dtype=torch.uint8, device=DEV),
+                    torch.full((cap, h // 128), oracle.SENTINEL_SCALE, dtype=torch.float32,
+                               device=DEV))
+
         sep = moe.moe_dispatch_layout(ids, e, 128)
-        res = moe.moe_dispatch(x, ids, sep.expand_idx, sep.ep_send_counts, e, capacity_rows=cap,
-                               out_dtype=dtype, status=sep.status)
-        fused = moe.moe_dispatch_fused(x, ids, e, 128, capacity_rows=cap, out_dtype=dtype)
+        sx, ss = buffers()
+        moe.moe_dispatch(x, ids, sep.expand_idx, sep.ep_send_counts, e, capacity_rows=cap,
+                         out_dtype=dtype, expand_x=sx, quant_scales=ss, status=sep.status)
+        fx, fs = buffers()
+        fused = moe.moe_dispatch_fused(x, ids, e, 128, capacity_rows=cap, out_dtype=dtype,
+                                       expand_x=fx, quant_scales=fs)
         torch.cuda.synchronize()
-        for a, b in zip(sep, fused[0]):
-            assert torch.equal(a, b)
+        for lay in (sep, fused[0]):
+            np.testing.assert_array_equal(lay.expert_counts.cpu().numpy(), c)
+            np.testing.assert_array_equal(lay.ep_send_counts.cpu().numpy(), s)
+            np.testing.assert_array_equal(lay.expand_idx.cpu().numpy(), r)
+            assert int(lay.status.cpu()[0]) == 0
         if dtype == "bf16":
-            slots = (sep.ep_send_counts[ids.reshape(-1).long()] + sep.expand_idx).long()
-            assert torch.equal(res[slots].view(torch.int16), fused[1][slots].view(torch.int16))
+            ref, f2 = oracle.dispatch_bf16(x_bits, ids_h, r, s, e, cap)
+            assert f2 == 0
+            np.testing.assert_array_equal(bits_of(sx), ref)
+            np.testing.assert_array_equal(bits_of(fx), ref)
         else:
-            slots = (sep.ep_send_counts[ids.reshape(-1).long()] + sep.expand_idx).long()
-            assert torch.equal(res[0][slots], fused[1][slots])
-            assert torch.equal(res[1][slots], fused[2][slots])
+            ref_q, ref_s, f2 = oracle.dispatch_fp8(x_bits, ids_h, r, s, e, cap)
+            assert f2 == 0
+            for q, sc in ((sx, ss), (fx, fs)):
+                np.testing.assert_array_equal(q.cpu().numpy(), ref_q)
+                np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32),
+                                              ref_s.view(np.uint32))
 
 
 @pytest.mark.parametrize("bs,h,e,k,align", [

@@ -5,8 +5,10 @@ bit-exact (both sides decide each code in fp32 with a correctly rounded
 division and round-to-nearest-even); combine within 1 bf16 ulp of the oracle
 (identical fp32 FMA order, so 0 is expected and asserted as well).  Small
 cases compare every element, including the untouched padding rows; the
-full-size workloads compare the whole layout, every dispatched row (against
-the oracle's slots) and a sample of combined tokens computed by the oracle.
+full-size workloads compare the whole layout, every dispatched row of the
+separate and the fused call (e4m3: the whole buffer against the oracle's;
+bf16: each row against its token's and every padding row against the
+sentinel) and every combined token against the oracle.
 """
 
 import numpy as np
@@ -400,77 +402,82 @@ def test_workload_full_size(name):
     x_d = inp["x"].to(DEV)
     slots = torch.from_numpy(s[ids.ravel()].astype(np.int64) + r).to(DEV)
     tok = torch.arange(w.bs, device=DEV).repeat_interleave(w.topk)
-    rng = np.random.default_rng(w.seed + 50)
-    sample = np.unique(np.concatenate([[0, w.bs - 1], rng.integers(0, w.bs, 62)]))
 
-    # dispatch
-    if w.fp8:
-        codes, qs = moe.moe_dispatch(x_d, ids_d, lay.expand_idx, lay.ep_send_counts, w.experts,
-                                     out_dtype="fp8", capacity_rows=cap)
-        torch.cuda.synchronize()
-        x_bits = workloads.bits(inp["x"])
-        s2 = slots.view(w.bs, w.topk).cpu().numpy()
-        codes_h = codes[slots.view(w.bs, w.topk)[torch.from_numpy(sample).to(DEV)]].cpu().numpy()
-        qs_h = qs[slots.view(w.bs, w.topk)[torch.from_numpy(sample).to(DEV)]].cpu().numpy()
-        for n, t in enumerate(sample):
-            q_ref, s_ref = oracle.quantize_row_e4m3(x_bits[t])
-            for j in range(w.topk):
-                np.testing.assert_array_equal(codes_h[n, j], q_ref)
-                np.testing.assert_array_equal(qs_h[n, j].view(np.uint32), s_ref.view(np.uint32))
-        # all K copies of every token identical (whole buffer)
-        sv = slots.view(w.bs, w.topk)
-        for j in range(1, w.topk):
-            assert torch.equal(codes[sv[:, j]], codes[sv[:, 0]])
-            assert torch.equal(qs[sv[:, j]], qs[sv[:, 0]])
-        rel, cmin, call = fp8_metrics_dev(codes, qs, x_d, sv[:, 0], torch.arange(w.bs,
-                                                                              device=DEV))
-        print(f"[workload {name}] fp8 max rel {rel:.6f} min row cos {cmin:.6f} "
-              f"cos {call:.6f}", flush=True)
-        assert rel <= 0.07 and cmin >= 0.999 and call >= 0.999
-        del s2
-    else:
-        ex = moe.moe_dispatch(x_d, ids_d, lay.expand_idx, lay.ep_send_counts, w.experts,
-                              capacity_rows=cap)
-        torch.cuda.synchronize()
-        # every dispatched row equals its token's row, bit for bit
-        assert torch.equal(ex[slots].view(torch.int16), x_d[tok].view(torch.int16))
+    # dispatch: the separate call and moe_dispatch_fused (the call the
+    # benchmark times: one launch for decode sizes; else the layout launches
+    # that read the rows ahead, then the scatter in its cache-resident or its
+    # full-occupancy shape), each into sentinel-filled buffers, so that every
+    # padding row must come back untouched
+    def sentinel_rows():
+        if w.fp8:
+            return (torch.full((cap, w.hidden), oracle.SENTINEL_FP8, dtype=torch.uint8,
+                               device=DEV),
+                    torch.full((cap, w.hidden // 128), oracle.SENTINEL_SCALE,
+                               dtype=torch.float32, device=DEV))
+        return (torch.full((cap, w.hidden), oracle.SENTINEL_BF16, dtype=torch.int16,
+                           device=DEV).view(torch.bfloat16), None)
 
-    # moe_dispatch_fused, the call the benchmark times (one launch for decode
-    # sizes; else layout launches that read the rows ahead, then the scatter
-    # in its cache-resident or its full-occupancy shape): the same layout and
-    # the same dispatched rows
+    kind = "fp8" if w.fp8 else "bf16"
+    ex, qs = sentinel_rows()
+    moe.moe_dispatch(x_d, ids_d, lay.expand_idx, lay.ep_send_counts, w.experts, out_dtype=kind,
+                     capacity_rows=cap, expand_x=ex, quant_scales=qs, check=True)
+    fx, fqs = sentinel_rows()
     fused = moe.moe_dispatch_fused(x_d, ids_d, w.experts, w.align, capacity_rows=cap,
-                                   out_dtype="fp8" if w.fp8 else "bf16")
+                                   out_dtype=kind, expand_x=fx, quant_scales=fqs, check=True)
     torch.cuda.synchronize()
     for a, b in zip(lay, fused[0]):
         assert torch.equal(a, b)
     if w.fp8:
-        assert torch.equal(fused[1][slots], codes[slots])
-        assert torch.equal(fused[2][slots], qs[slots])
+        # every code and scale of the whole buffer, against the oracle's
+        # quantisation of each token (padding rows: the sentinels)
+        codes_ref, qs_ref, fl = oracle.dispatch_fp8(workloads.bits(inp["x"]), ids, r, s,
+                                                    w.experts, cap)
+        assert fl == 0
+        for what, codes, scales in (("dispatch", ex, qs), ("fused", fx, fqs)):
+            np.testing.assert_array_equal(codes.cpu().numpy(), codes_ref, err_msg=what)
+            np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32),
+                                          qs_ref.view(np.uint32), err_msg=what)
+        sv = slots.view(w.bs, w.topk)
+        rel, cmin, call = fp8_metrics_dev(fx, fqs, x_d, sv[:, 0], torch.arange(w.bs, device=DEV))
+        print(f"[workload {name}] fp8 max rel {rel:.6f} min row cos {cmin:.6f} "
+              f"cos {call:.6f}", flush=True)
+        assert rel <= 0.07 and cmin >= 0.999 and call >= 0.999
+        del codes_ref, qs_ref
     else:
-        assert torch.equal(fused[1][slots].view(torch.int16), x_d[tok].view(torch.int16))
-    del fused
+        # every dispatched row equals its token's row, bit for bit, and every
+        # other row still holds the sentinel
+        pad = torch.ones(cap, dtype=torch.bool, device=DEV)
+        pad[slots] = False
+        for what, rows in (("dispatch", ex), ("fused", fx)):
+            assert torch.equal(rows[slots].view(torch.int16), x_d[tok].view(torch.int16)), what
+            assert bool((rows.view(torch.int16)[pad] == oracle.SENTINEL_BF16).all()), what
+        del pad
+    del fused, fx, fqs
 
-    # combine
+    # combine: every token against the oracle (at the large workload this
+    # includes every token with a row past 2^31 bytes into y)
     if w.identity_experts:
         y_d = ex
         y_bits = oracle.dispatch_bf16(workloads.bits(inp["x"]), ids, r, s, w.experts, cap)[0]
     else:
         y_d = inp["y"].to(DEV)
         y_bits = workloads.bits(inp["y"])
+    row_bytes = 2 * w.hidden
+    far = int((torch.from_numpy(s[ids.ravel()].astype(np.int64) + r) * row_bytes
+               >= 2 ** 31).view(w.bs, w.topk).any(1).sum())
+    print(f"[workload {name}] tokens with a row past 2^31 bytes: {far}", flush=True)
     sh = inp["shared"]
     sh_d = None if sh is None else sh.to(DEV)
     out = moe.moe_combine(y_d, ids_d, lay.expand_idx, lay.ep_send_counts, dev(sc), sh_d,
-                          w.experts)
+                          w.experts, check=True)
     torch.cuda.synchronize()
-    got = host_bits(out[torch.from_numpy(sample).to(DEV)])
-    ref, _ = oracle.combine(y_bits, ids[sample], r.reshape(w.bs, w.topk)[sample].ravel(), s,
-                            sc[sample], None if sh is None else workloads.bits(sh)[sample],
-                            w.experts)
-    assert ulp_diff(got, ref).max() <= 1
+    got = host_bits(out)
+    ref, fl = oracle.combine(y_bits, ids, r, s, sc, None if sh is None else workloads.bits(sh),
+                             w.experts)
+    assert fl == 0
     np.testing.assert_array_equal(got, ref)
     if w.identity_experts:
-        np.testing.assert_array_equal(oracle.bf16_bits_to_f32(host_bits(out)),
+        np.testing.assert_array_equal(oracle.bf16_bits_to_f32(got),
                                       oracle.bf16_bits_to_f32(workloads.bits(inp["x"])))
 
 
