@@ -139,13 +139,14 @@ __global__ __launch_bounds__(THREADS) void dispatch_bf16_kernel(
 // Each thread owns 16 consecutive channels (two 16-byte loads of bf16, one
 // 16-byte store of e4m3 codes); 8 neighbouring lanes form one 128-channel
 // scale block and combine their maxima with cross-lane exchanges.
-template <int THREADS, int KMAX, bool DEFER>
+template <int THREADS, int KMAX, bool DEFER, int LDS_INTS>
 __global__ __launch_bounds__(THREADS) void dispatch_fp8_kernel(
     const u32x4* x, int64_t xs, int32_t ngroups, int32_t nchunks,
     const int32_t* __restrict__ ids, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ send, int32_t k, int32_t E, u32x4* __restrict__ out, int64_t os,
     float* __restrict__ scales, int32_t nblk, int64_t cap, int32_t* status, DeferredRanks dr) {
-  __shared__ int lds[RouteTables<THREADS, DEFER>::kInts];
+  static_assert(LDS_INTS >= RouteTables<THREADS, DEFER>::kInts, "tables must fit");
+  __shared__ int lds[LDS_INTS];
   const int32_t t = blockIdx.x / nchunks;
   const int32_t chunk = blockIdx.x - t * nchunks;
   PairMeta meta;
@@ -230,13 +231,26 @@ hipError_t launch_bf16_shape(const void* x, int64_t x_stride, int32_t bs, int32_
   return hipGetLastError();
 }
 
+// LDS ints per workgroup such that `per_cu` workgroups fit a compute
+// unit's 160 KB and one more does not (in 512-byte steps).
+constexpr int lds_ints_for(int per_cu) { return (163840 / per_cu) / 512 * 512 / 4; }
+
+#ifndef MOE_FP8_PER_CU
+#define MOE_FP8_PER_CU 0   // e4m3 scatter workgroups per compute unit (0: no LDS cap)
+#endif
+constexpr int kFp8PerCu = MOE_FP8_PER_CU;
+#ifndef MOE_FP8_SCATTER_THREADS
+#define MOE_FP8_SCATTER_THREADS MOE_FP8_THREADS   // threads per e4m3 scatter workgroup
+#endif
+constexpr int kFp8Threads = MOE_FP8_SCATTER_THREADS;
+
 template <bool DEFER>
 hipError_t launch_fp8_shape(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
                             const int32_t* ids, const int32_t* expand_idx, const int32_t* send,
                             int32_t k, int32_t num_experts, void* expand_x,
                             int64_t expand_x_stride, int64_t capacity_rows, float* quant_scales,
                             int32_t* status, hipStream_t stream, const DeferredRanks& dr) {
-  constexpr int kThreads = MOE_FP8_THREADS;
+  constexpr int kThreads = kFp8Threads;
   const int32_t ngroups = hidden / 16;
   const int32_t nchunks = (ngroups + kThreads - 1) / kThreads;
   const int32_t n_items = bs * nchunks;
@@ -245,34 +259,23 @@ hipError_t launch_fp8_shape(const void* x, int64_t x_stride, int32_t bs, int32_t
   u32x4* ov = static_cast<u32x4*>(expand_x);
   const int64_t xs = x_stride / 8, os = expand_x_stride / 16;
   const int32_t nblk = hidden / 128;
+  constexpr int kTables = RouteTables<kThreads, DEFER>::kInts;
+  constexpr int kLds = kFp8PerCu > 0 && lds_ints_for(kFp8PerCu) > kTables
+                           ? lds_ints_for(kFp8PerCu) : kTables;
+#define MOE_SCATTER(KM)                                                                     \
+  launch_kernel(dispatch_fp8_kernel<kThreads, KM, DEFER, kLds>, grid, kThreads, stream, xv, \
+      xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os, quant_scales,    \
+      nblk, capacity_rows, status, dr)
   switch (kmax_for(k)) {
-    case 2:
-      launch_kernel(dispatch_fp8_kernel<kThreads, 2, DEFER>, grid, kThreads, stream,
-          xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          quant_scales, nblk, capacity_rows, status, dr);
-      break;
-    case 4:
-      launch_kernel(dispatch_fp8_kernel<kThreads, 4, DEFER>, grid, kThreads, stream,
-          xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          quant_scales, nblk, capacity_rows, status, dr);
-      break;
-    case 8:
-      launch_kernel(dispatch_fp8_kernel<kThreads, 8, DEFER>, grid, kThreads, stream,
-          xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          quant_scales, nblk, capacity_rows, status, dr);
-      break;
-    default:
-      launch_kernel(dispatch_fp8_kernel<kThreads, 16, DEFER>, grid, kThreads, stream,
-          xv, xs, ngroups, nchunks, ids, expand_idx, send, k, num_experts, ov, os,
-          quant_scales, nblk, capacity_rows, status, dr);
-      break;
+    case 2: MOE_SCATTER(2); break;
+    case 4: MOE_SCATTER(4); break;
+    case 8: MOE_SCATTER(8); break;
+    default: MOE_SCATTER(16); break;
   }
+#undef MOE_SCATTER
   return hipGetLastError();
 }
 
-// LDS ints per workgroup such that `per_cu` workgroups fit a compute
-// unit's 160 KB and one more does not (in 512-byte steps).
-constexpr int lds_ints_for(int per_cu) { return (163840 / per_cu) / 512 * 512 / 4; }
 
 #ifndef MOE_CACHED_ROWS_PER_CU
 #define MOE_CACHED_ROWS_PER_CU 7   // workgroups of the cache-resident scatter per compute unit
