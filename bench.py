@@ -15,10 +15,10 @@ by the measured step time, in GB/s; `tokens_per_s` is tokens per step over the
 same time.  The timed region holds the steps alone: no event is bound to a
 launch inside it.  The `roofline` object covers the kernel that moves the most
 bytes (combine): its algorithmic bytes per launch over its mean kernel time,
-from HIP events bound to the combine launch (moe_time_next_launches: the
-runtime stamps them with the kernel's own start and end on the launch stream)
-in ROOFLINE_STEPS steps after the timed region.  `kernels_ms` adds the layout
-and dispatch kernels, each launch timed the same way in 10 further steps.
+from HIP events bound to every launch (moe_time_next_launches: the runtime
+stamps them with the kernel's own start and end on the launch stream) in
+ROOFLINE_STEPS steps after the timed region; `kernels_ms` gives every
+kernel's mean from the same steps.
 
 `--separate` runs layout and dispatch as two calls (moe_dispatch_layout,
 moe_dispatch); `--graph` replays the steps as captured HIP graphs of 10 steps
@@ -41,8 +41,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
 GRAPH_STEPS = 10        # steps per captured graph (--graph)
-ROOFLINE_STEPS = 20     # steps after the timed region whose combine launch is timed
-BREAKDOWN_STEPS = 10    # steps after those with every kernel launch timed
+ROOFLINE_STEPS = 20     # steps after the timed region with every kernel launch timed
 METRIC = "dispatch+combine achieved HBM GB/s and tokens/s, H=7168 E=256 K=8 bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_bf16_skewed_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_moe_dispatch_layout_amd", "csrc", f)
@@ -336,10 +335,12 @@ def layout_sweep(moe):
     return out
 
 
-def practical_ceiling(moe, w, slots, cap, launches=16):
+def practical_ceiling(moe, w, slots, cap, out_row_bytes, launches=16):
     """GB/s of the plain streaming probe with the dispatch's 1 : K and the
     combine's (K + 1) : 1 row mixes at this workload's bf16 row size and
-    token count, with the expert-side rows
+    token count, and of the scatter's writes alone (`scatter_writes`: K rows
+    of `out_row_bytes` per token, the row read being one cache-resident row,
+    write bytes counted), with the expert-side rows
       - in order (`in_order`),
       - randomly permuted (`random_rows`; seeded), and
       - at the real layout's slots of this routing (`layout_rows`: tokens in
@@ -356,16 +357,23 @@ def practical_ceiling(moe, w, slots, cap, launches=16):
     rows_y = max(bs * k, cap)
     layout_rows = slots.to(torch.int32).contiguous()
     out = {}
-    for name, reads, writes in (("dispatch_mix", 1, k), ("combine_mix", k + 1, 1)):
-        src = torch.zeros((bs if writes > 1 else rows_y + bs, cols), dtype=torch.int32,
+    one_row = torch.zeros(bs, dtype=torch.int32, device="cuda")
+    for name, reads, writes in (("dispatch_mix", 1, k), ("combine_mix", k + 1, 1),
+                                ("scatter_writes", 1, k)):
+        mix_cols = out_row_bytes // 4 if name == "scatter_writes" else cols
+        src_n = 1 if name == "scatter_writes" else (bs if writes > 1 else rows_y + bs)
+        src = torch.zeros((src_n, mix_cols), dtype=torch.int32, device="cuda")
+        dst = torch.empty((rows_y if writes > 1 else bs, mix_cols), dtype=torch.int32,
                           device="cuda")
-        dst = torch.empty((rows_y if writes > 1 else bs, cols), dtype=torch.int32, device="cuda")
         perm = torch.from_numpy(g.permutation(bs * k).astype(np.int32)).cuda().view(bs, k)
         shared_rows = (rows_y + torch.arange(bs, dtype=torch.int32, device="cuda"))[:, None]
         res = {}
         for order, expert_rows in (("in_order", None), ("random_rows", perm),
                                    ("layout_rows", layout_rows)):
-            if expert_rows is None:   # contiguous: item i's rows i*R .. i*R+R-1
+            if name == "scatter_writes":  # one cached source row, K rows written
+                src_rows = one_row
+                dst_rows = None if expert_rows is None else expert_rows.reshape(-1).contiguous()
+            elif expert_rows is None:   # contiguous: item i's rows i*R .. i*R+R-1
                 src_rows = dst_rows = None
             elif writes > 1:          # dispatch: token row t, K copies to the expert rows
                 src_rows, dst_rows = None, expert_rows.reshape(-1).contiguous()
@@ -386,7 +394,9 @@ def practical_ceiling(moe, w, slots, cap, launches=16):
                 run()
             torch.cuda.synchronize()
             secs = sum(a.elapsed_time(z) for a, z in pairs) / 1e3 / launches
-            res[order] = round(bs * (reads + writes) * row_bytes / secs / 1e9, 1)
+            moved = (bs * writes * out_row_bytes if name == "scatter_writes"
+                     else bs * (reads + writes) * row_bytes)
+            res[order] = round(moved / secs / 1e9, 1)
         out[name] = res
         del src, dst
     torch.cuda.empty_cache()
@@ -527,16 +537,8 @@ def main():
         dispatch(b, lay)
         return lay
 
-    def step(b, pair=None):
-        """One step.  With `pair`, the combine launch takes that (start,
-        stop) event pair, stamped with the kernel's own start and end
-        (moe_time_next_launches)."""
-        lay = front(b)
-        if pair is not None:
-            moe.moe_time_next_launches([pair])
-        combine(b, lay)
-        if pair is not None and moe.moe_time_unused_launches():
-            raise SystemExit("the combine launched no kernel")
+    def step(b):
+        combine(b, front(b))
 
     def breakdown_step(b, pairs):
         """One step with every kernel launch taking one of `pairs`; returns
@@ -620,24 +622,17 @@ def main():
     elapsed = time.perf_counter() - t0
     gpu_ms_per_step = region[0].elapsed_time(region[1]) / args.steps
 
-    # Roofline: ROOFLINE_STEPS eager steps after the timed region, the
-    # combine launch of each bound to its own event pair (a bound launch
-    # costs its step a few microseconds of host and queue time, which is why
-    # none sits inside the timed region).
-    rl_pairs = new_pairs(ROOFLINE_STEPS)
-    torch.cuda.synchronize()
-    for i in range(ROOFLINE_STEPS):
-        step(bufs[(args.steps + i) % sets], rl_pairs[i])
-    torch.cuda.synchronize()
-    com_ms = [a.elapsed_time(z) for a, z in rl_pairs]
-
-    # Per-kernel split: BREAKDOWN_STEPS eager steps after those, every launch
-    # timed by its own bound events.
-    steps_taken = [breakdown_step(bufs[i % sets], new_pairs(16))
-                   for i in range(BREAKDOWN_STEPS)]
+    # Kernel times: ROOFLINE_STEPS eager steps after the timed region, every
+    # launch of each bound to its own event pair, stamped with the kernel's
+    # own start and end (a bound launch costs its step a few microseconds of
+    # host and queue time, which is why none sits inside the timed region).
+    # The roofline takes the combine launches of these steps.
+    steps_taken = [breakdown_step(bufs[(args.steps + i) % sets], new_pairs(16))
+                   for i in range(ROOFLINE_STEPS)]
     torch.cuda.synchronize()
     per_step = [split_kernels(t) for t in steps_taken]
     kern_ms = {r: [d[r] for d in per_step] for r in per_step[0] if r != "layout_launches"}
+    com_ms = kern_ms["combine"]
     mean = lambda v: sum(v) / len(v)
 
     def pct(v):
@@ -701,9 +696,8 @@ def main():
                    "ep_world_size": args.ep or None,
                    "bytes_per_step": step_bytes},
         "gpu_ms_per_step": round(gpu_ms_per_step, 4),
-        "kernel_times": (f"events bound to each launch (kernel start to end), after the timed "
-                         f"region: the combine in {ROOFLINE_STEPS} steps, every kernel in "
-                         f"{BREAKDOWN_STEPS} steps after those"),
+        "kernel_times": (f"events bound to each launch (kernel start to end) in "
+                         f"{ROOFLINE_STEPS} eager steps after the timed region"),
         "layout_launches": per_step[0].get("layout_launches", 0),
         "kernels_ms": {r: round(mean(v), 4) for r, v in kern_ms.items()},
         "kernels_gbs": {r: round(role_bytes[r] / mean(v) / 1e6, 1) for r, v in kern_ms.items()
@@ -711,7 +705,7 @@ def main():
         "kernels_us_p10_p50_p90": {r: pct(v) for r, v in kern_ms.items()},
         "roofline": {"kernel": "combine_fp8" if fp8_combine else "combine", "bound": "hbm",
                      "timed_launches": len(com_ms),
-                     "timing": (f"HIP events bound to the combine launch (kernel start to end) "
+                     "timing": (f"HIP events bound to every launch (kernel start to end) "
                                 f"in {ROOFLINE_STEPS} eager steps after the timed region"),
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -720,17 +714,23 @@ def main():
                      "traffic_unit": "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
                      "algorithmic_bytes_per_launch": nbytes["combine"],
                      "us_p10_p50_p90": pct(com_ms),
-                     "breakdown_combine_us": round(mean(kern_ms["combine"]) * 1e3, 2),
                      "step_achieved": round(step_gbs, 1),
                      "step_frac": round(step_gbs / HBM_PEAK_GBS, 4)},
     }
-    # The probe models bf16 rows at bandwidth-bound sizes (a decode-sized
-    # step is launch-latency bound, and a probe of it says nothing).
-    if not (args.no_ceiling or w.fp8 or fp8_combine or step_bytes < MALL_BYTES):
+    # The probe models bandwidth-bound sizes (a decode-sized step is launch-
+    # latency bound, and a probe of it says nothing) with bf16 rows read by
+    # the combine.
+    if not (args.no_ceiling or fp8_combine or step_bytes < MALL_BYTES):
         lay0 = bufs[0]["layout"]
         slots = (lay0.ep_send_counts[route_ids.reshape(-1).long()].long()
                  + lay0.expand_idx.long()).view(w.bs, w.topk)
-        ceil = practical_ceiling(moe, w, slots, cap)
+        out_row = w.hidden if w.fp8 else 2 * w.hidden
+        ceil = practical_ceiling(moe, w, slots, cap, out_row)
+        # The scatter's write rate: its row bytes (e4m3: codes and scales)
+        # over its kernel time.
+        row_w = out_row + (w.hidden // 128 * 4 if w.fp8 else 0)
+        scatter_gbs = w.bs * w.topk * row_w / (mean(kern_ms["dispatch"]) / 1e3) / 1e9 \
+            if "dispatch" in kern_ms else None
         result["practical_ceiling"] = {
             "probe": "moe_probe_stream_mix: plain 16-B streaming kernel, same read:write row mix",
             "unit": "GB/s", **ceil,
@@ -743,7 +743,10 @@ def main():
                 / ceil["dispatch_mix"]["random_rows"], 4) if not args.fused else None,
             "dispatch_frac_of_layout_rows": round(
                 nbytes["dispatch"] / (mean(kern_ms["dispatch"]) / 1e3) / 1e9
-                / ceil["dispatch_mix"]["layout_rows"], 4) if not args.fused else None}
+                / ceil["dispatch_mix"]["layout_rows"], 4) if not args.fused else None,
+            "scatter_write_gbs": None if scatter_gbs is None else round(scatter_gbs, 1),
+            "scatter_writes_frac_of_layout_rows": None if scatter_gbs is None else round(
+                scatter_gbs / ceil["scatter_writes"]["layout_rows"], 4)}
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
         cores = min(16, len(os.sched_getaffinity(0)))
