@@ -8,7 +8,7 @@ ranks, the bf16 scatter into the expert-contiguous, 128-row-padded buffer
 already resident in HBM when the timed region starts.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload skewed]
-                    [--separate] [--graph]
+                    [--separate] [--eager]
 
 `value` is algorithmic bytes per step (real rows only, never padding) divided
 by the measured step time, in GB/s; `tokens_per_s` is tokens per step over the
@@ -20,9 +20,11 @@ stamps them with the kernel's own start and end on the launch stream) in
 ROOFLINE_STEPS steps after the timed region; `kernels_ms` gives every
 kernel's mean from the same steps.
 
+The timed steps are replayed as captured HIP graphs of up to 10 steps each
+(the largest count that divides --steps), the way a serving loop replays a
+layer's launches; `--eager` launches every kernel from the host instead.
 `--separate` runs layout and dispatch as two calls (moe_dispatch_layout,
-moe_dispatch); `--graph` replays the steps as captured HIP graphs of 10 steps
-each.  `cpu_baseline` times the CPU oracle on the same workload.
+moe_dispatch).  `cpu_baseline` times the CPU oracle on the same workload.
 """
 
 from __future__ import annotations
@@ -40,7 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
-GRAPH_STEPS = 10        # steps per captured graph (--graph)
+GRAPH_STEPS = 10        # most steps per captured graph
 ROOFLINE_STEPS = 20     # steps after the timed region with every kernel launch timed
 METRIC = "dispatch+combine achieved HBM GB/s and tokens/s, H=7168 E=256 K=8 bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_bf16_skewed_traffic.txt")
@@ -77,9 +79,9 @@ def parse():
                    help="layout + dispatch through moe_dispatch_fused (the default; one launch "
                         "for batches of at most 2048 pairs, else the layout launches read the "
                         "token rows ahead for the scatter)")
-    p.add_argument("--graph", action="store_true",
-                   help="replay the steps as captured HIP graphs of 10 steps instead of eager "
-                        "launches")
+    p.add_argument("--eager", action="store_true",
+                   help="launch the timed steps' kernels from the host instead of replaying "
+                        "captured HIP graphs")
     p.add_argument("--no-ceiling", action="store_true",
                    help="skip the practical-ceiling probe (streaming kernels with the "
                         "dispatch's and combine's read:write mixes)")
@@ -584,23 +586,21 @@ def main():
     torch.cuda.synchronize()
 
     graphs = None
-    if args.graph:
-        # Steps are captured GRAPH_STEPS at a time, the way a serving loop
+    per_graph = max(d for d in range(1, GRAPH_STEPS + 1) if args.steps % d == 0)
+    if not args.eager:
+        # Steps are captured per_graph at a time, the way a serving loop
         # replays a whole pass; one graph per distinct sequence of buffer
         # sets.  No call allocates or enqueues a memset when its outputs are
-        # given.
-        if args.steps % GRAPH_STEPS:
-            print(f"--graph needs --steps to be a multiple of {GRAPH_STEPS}", file=sys.stderr)
-            sys.exit(2)
+        # given.  Each graph is replayed once before the timed region.
         graphs = []
-        for c in range(sets // math.gcd(sets, GRAPH_STEPS)):
+        for c in range(sets // math.gcd(sets, per_graph)):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for j in range(GRAPH_STEPS):
-                    step(bufs[(c * GRAPH_STEPS + j) % sets])
+                for j in range(per_graph):
+                    step(bufs[(c * per_graph + j) % sets])
             graphs.append(g)
         for g in graphs:
-            g.replay()
+            g.replay()   # counted in warmup_steps_run
         torch.cuda.synchronize()
 
     # Timed region: exactly K steps on the host clock, synchronised on both
@@ -615,7 +615,7 @@ def main():
         for i in range(args.steps):
             step(bufs[i % sets])
     else:
-        for c in range(args.steps // GRAPH_STEPS):
+        for c in range(args.steps // per_graph):
             graphs[c % len(graphs)].replay()
     region[1].record(stream)
     torch.cuda.synchronize()
@@ -670,7 +670,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "warmup_steps_run": warmup_run,
+        "warmup_steps_run": warmup_run + (len(graphs) * per_graph if graphs else 0),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -686,7 +686,7 @@ def main():
                                                            if w.routing == "zipf" else ""),
                    "align": w.align, "capacity_rows": cap, "buffer_sets": sets,
                    "x_bytes_between_reuse": 2 * w.bs * w.hidden * (sets - 1),
-                   "launch": (f"hip graphs of {GRAPH_STEPS} steps" if args.graph else "eager"),
+                   "launch": ("eager" if args.eager else f"hip graphs of {per_graph} steps"),
                    "layout_dispatch": (("moe_dispatch_fused_replicated" if args.replicas > 0
                                         else "moe_dispatch_fused") if args.fused
                                        else "separate"),
