@@ -20,7 +20,7 @@ stamps them with the kernel's own start and end on the launch stream) in
 ROOFLINE_STEPS steps after the timed region; `kernels_ms` gives every
 kernel's mean from the same steps.
 
-The timed steps are replayed as captured HIP graphs of up to 10 steps each
+The timed steps are replayed as captured HIP graphs of up to 20 steps each
 (the largest count that divides --steps), the way a serving loop replays a
 layer's launches; `--eager` launches every kernel from the host instead.
 `--separate` runs layout and dispatch as two calls (moe_dispatch_layout,
@@ -42,7 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
-GRAPH_STEPS = 10        # most steps per captured graph
+GRAPH_STEPS = 20        # most steps per captured graph (a pass of 20 MoE layers)
 ROOFLINE_STEPS = 20     # steps after the timed region with every kernel launch timed
 METRIC = "dispatch+combine achieved HBM GB/s and tokens/s, H=7168 E=256 K=8 bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_bf16_skewed_traffic.txt")
