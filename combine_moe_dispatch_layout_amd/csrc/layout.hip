@@ -85,15 +85,17 @@ __device__ void write_counts_and_offsets(int c, int32_t E, int32_t align, int* w
   }
 }
 
-// Flags an expert (an id in [0, E)) repeated within one of the tokens whose
-// first pair lies in [begin, end).
-__device__ __forceinline__ int duplicate_flags(const int32_t* __restrict__ ids, int32_t k,
-                                               int32_t E, int64_t begin, int64_t end) {
+// Flags an expert (an id in [0, E)) repeated within one of the chunk's
+// tokens, from the chunk's ids staged in LDS (`chunk_ids[i]` = id of the
+// chunk's pair i; the chunk holds whole tokens).  One token per thread, its
+// K ids compared in registers.
+__device__ __forceinline__ int duplicate_flags(const int* chunk_ids, int32_t n, int32_t k,
+                                               int32_t E) {
   int fl = 0;
-  for (int64_t t = (begin + k - 1) / k + (int)threadIdx.x; t * k < end; t += kLayoutThreads) {
+  for (int base = (int)threadIdx.x * k; base < n; base += kLayoutThreads * k) {
     int v[kMaxTopK];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) v[j] = (j < k) ? ids[t * k + j] : -1 - j;
+    for (int j = 0; j < kMaxTopK; ++j) v[j] = (j < k) ? chunk_ids[base + j] : -1 - j;
 #pragma unroll
     for (int a = 1; a < kMaxTopK; ++a)
 #pragma unroll
@@ -134,9 +136,22 @@ __device__ void finish_layout(const LayoutScratch& ws, int32_t blocks, int32_t E
   const bool active = col < E;
   int32_t* __restrict__ h = ws.hist;
 
+  // Each workgroup's flag word is one thread's (at most kLayoutMaxBlocks <
+  // kLayoutThreads workgroups); its load is issued with pass 1's.
+  static_assert(kLayoutMaxBlocks <= kLayoutThreads, "one flag word per thread");
+  const int f = (tid < blocks) ? ws.flags[tid] : 0;
   // Pass 1: this thread's partial column sum, 16 independent loads at a time.
+  // A run of at most 16 rows (every run when blocks <= 16 * groups) stays in
+  // registers for pass 2.
+  const bool fits = r1 - r0 <= 16;
   int partial = 0;
-  if (active) {
+  int kept[16];
+  if (active && fits) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) kept[u] = (r0 + u < r1) ? h[(int64_t)(r0 + u) * E + col] : 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) partial += kept[u];
+  } else if (active) {
     for (int b0 = r0; b0 < r1; b0 += 16) {
       int v[16];
 #pragma unroll
@@ -147,8 +162,6 @@ __device__ void finish_layout(const LayoutScratch& ws, int32_t blocks, int32_t E
     }
   }
   part[tid] = partial;
-  int f = 0;
-  for (int b = tid; b < blocks; b += kLayoutThreads) f |= ws.flags[b];
   if (f) atomicOr(flags_lds, f);
   __syncthreads();
   int run = 0, total = 0;
@@ -158,7 +171,13 @@ __device__ void finish_layout(const LayoutScratch& ws, int32_t blocks, int32_t E
     total += p;
   }
   // Pass 2: the exclusive prefix down the column, written over the counts.
-  if (active) {
+  if (active && fits) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (r0 + u < r1) h[(int64_t)(r0 + u) * E + col] = run;
+      run += kept[u];
+    }
+  } else if (active) {
     for (int b0 = r0; b0 < r1; b0 += 16) {
       int v[16];
 #pragma unroll
@@ -201,6 +220,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
   }
   __shared__ unsigned long long mask[kLayoutWaves][kMaxExperts];  // 32 KB
   __shared__ int wave_run[kLayoutWaves][kMaxExperts];             // 16 KB
+  __shared__ int chunk_ids[kLayoutThreads * R];  // the chunk's input ids, for repeats
   __shared__ int blk_run[kMaxExperts];   // pairs per expert in earlier chunks
   __shared__ int rep_off[kMaxExperts + 1];
   __shared__ uint32_t rep_thr[kMaxExperts];
@@ -239,10 +259,18 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     for (int j = tid; j <= n_ids; j += kLayoutThreads) rep_off[j] = map.offsets[j];
     for (int j = tid; j < E; j += kLayoutThreads) rep_thr[j] = map.thresholds[j];
   }
-  int fl = duplicate_flags(ids, k, n_ids, bbegin, bend);
+  int fl = 0;
   __syncthreads();
 
   const unsigned long long below_me = (1ull << lane) - 1ull;
+  // Repeated experts within a token: when K divides the wave, every chunk's
+  // 64-pair sub-rounds hold whole tokens, so a repeat shows in the expert's
+  // lane mask as a second bit among the token's K lanes.  Otherwise (and for
+  // repeats of logical experts under a replica map) the chunk's ids are
+  // staged in LDS and each token's K ids compared.
+  const bool mask_dups = !mapped && kWave % k == 0;
+  const unsigned long long token_lanes =
+      (k >= kWave ? ~0ull : ((1ull << k) - 1ull)) << (lane - lane % k);
   for (int c = 0; c < chunks; ++c) {
     const int64_t begin = bbegin + (int64_t)c * chunk_pairs;
     if (begin >= bend) break;  // workgroup-uniform
@@ -253,6 +281,13 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
       for (int s = 0; s < R; ++s) {
         const int64_t i = wbase + s * kWave + lane;
         e[s] = (i < end) ? ids[i] : 0;
+      }
+    }
+    if (!mask_dups) {
+#pragma unroll
+      for (int s = 0; s < R; ++s) {
+        const int64_t i = wbase + s * kWave + lane;
+        if (i < end) chunk_ids[i - begin] = e[s];  // as given, before any replica mapping
       }
     }
 
@@ -296,6 +331,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
       }
       __builtin_amdgcn_wave_barrier();
       const int below = __popcll(m & below_me);
+      if (mask_dups && ok && __popcll(m & token_lanes) > 1) fl |= MOE_FLAG_DUP_ID;
       lr[s] = ok ? before + below : -1;
       if (ok && below == 0) {
         wave_run[wave][e[s]] = before + __popcll(m);
@@ -304,6 +340,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
       __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
+    if (!mask_dups) fl |= duplicate_flags(chunk_ids, (int32_t)(end - begin), k, n_ids);
 
     // Exclusive prefix over waves, per expert, after the earlier chunks.
     int run = 0;

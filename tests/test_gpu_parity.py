@@ -114,8 +114,12 @@ def test_layout_edge_cases():
 
 
 def test_layout_invalid_and_repeated_ids():
+    """Out-of-range and repeated ids, with K dividing the 64-lane wave (repeats
+    found in the ranking's lane masks) and not (found from the chunk's ids
+    staged in LDS), in one-workgroup and multi-workgroup layouts."""
     rng = np.random.default_rng(102)
-    for bs, e, k in [(50, 8, 3), (3000, 100, 6)]:
+    for bs, e, k in [(50, 8, 3), (3000, 100, 6), (64, 16, 1), (700, 64, 8), (5000, 256, 8),
+                     (300, 32, 16), (9000, 16, 2), (2000, 64, 4), (40000, 512, 16)]:
         ids = random_ids(rng, bs, e, k)
         bad = rng.random(ids.shape) < 0.05
         ids[bad] = rng.choice([-1, e, e + 7, -1000], size=bad.sum())
@@ -123,8 +127,11 @@ def test_layout_invalid_and_repeated_ids():
         assert f & oracle.FLAG_ID_RANGE
         ids2 = random_ids(rng, bs, e, k)
         ids2[::7, -1] = ids2[::7, 0]
+        if k > 2:
+            ids2[3::11, 1] = ids2[3::11, 0]  # three copies of one expert in some tokens
+            ids2[3::11, 2] = ids2[3::11, 0]
         (c, s, r, f), _ = assert_layout_equal(ids2, e, 128)
-        assert f == oracle.FLAG_DUP_ID
+        assert f == (oracle.FLAG_DUP_ID if k > 1 else 0)
 
 
 def test_layout_is_deterministic():
