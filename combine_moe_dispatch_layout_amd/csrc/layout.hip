@@ -360,13 +360,15 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
       const int64_t i = wbase + s * kWave + lane;
       if (i < end) ranks_out[i] = lr[s] >= 0 ? lr[s] + wave_run[wave][e[s]] : -1;
     }
-    __syncthreads();
-    if (tid < E) {
-      blk_run[tid] = run;
+    if (tid < E) blk_run[tid] = run;  // read back below only by the same thread
+    if (end < bend) {  // another chunk follows (workgroup-uniform)
+      __syncthreads();
+      if (tid < E) {
 #pragma unroll
-      for (int w = 0; w < kLayoutWaves; ++w) wave_run[w][tid] = 0;
+        for (int w = 0; w < kLayoutWaves; ++w) wave_run[w][tid] = 0;
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
   if (fl) atomicOr(&flags_lds, fl);
   __syncthreads();
