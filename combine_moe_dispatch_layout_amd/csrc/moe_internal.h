@@ -306,7 +306,10 @@ constexpr int64_t kSerialMinItems = 8192;
 #endif
 constexpr int kReadAheadMaxBlocks = MOE_READ_AHEAD_BLOCKS;
 constexpr int64_t kReadAheadMaxBytes = int64_t(128) << 20;
-constexpr int kReadAheadUnroll = 16;      // loads in flight per thread
+// Loads in flight per read-ahead thread: enough to keep HBM busy, few enough
+// that the ranking workgroups' own loads in the same launch do not queue
+// behind a deep backlog.
+constexpr int kReadAheadUnroll = 4;
 
 // Body of a read-ahead workgroup: block `blockIdx.x - first_block` of
 // `blocks` reads its share of vectors [lo, hi).  Nothing is stored; the
