@@ -77,7 +77,7 @@ def parse():
                         "moe_dispatch_fused or moe_dispatch_fused_replicated")
     p.add_argument("--fused", action="store_true",
                    help="layout + dispatch through moe_dispatch_fused (the default; one launch "
-                        "for batches of at most 2048 pairs, else the layout launches read the "
+                        "for batches of at most 2048 pairs, else the layout launch reads the "
                         "token rows ahead for the scatter)")
     p.add_argument("--eager", action="store_true",
                    help="launch the timed steps' kernels from the host instead of replaying "
@@ -237,6 +237,12 @@ def buffer_sets(w, cap, step_bytes, fp8_combine):
     by_cache = 1 + -(-2 * MALL_BYTES // x_bytes)
     by_volume = -(-(2 << 30) // step_bytes)
     return max(1, min(max(by_cache, by_volume), SET_MEMORY_CAP // per_set, 64))
+
+
+def steps_per_graph(steps: int) -> int:
+    """Steps per captured graph: the largest count up to GRAPH_STEPS that
+    divides the timed steps, so that the timed region replays whole graphs."""
+    return max(d for d in range(1, GRAPH_STEPS + 1) if steps % d == 0)
 
 
 def per_launch_in_graphs(fn, launches=10, replays=30):
@@ -586,7 +592,7 @@ def main():
     torch.cuda.synchronize()
 
     graphs = None
-    per_graph = max(d for d in range(1, GRAPH_STEPS + 1) if args.steps % d == 0)
+    per_graph = steps_per_graph(args.steps)
     if not args.eager:
         # Steps are captured per_graph at a time, the way a serving loop
         # replays a whole pass; one graph per distinct sequence of buffer
@@ -646,7 +652,7 @@ def main():
         raise SystemExit(f"layout status flags {status}: routing is invalid")
 
     combine_s = mean(com_ms) / 1e3
-    # When moe_dispatch_fused's layout launches read the token rows ahead,
+    # When moe_dispatch_fused's layout launch reads the token rows ahead,
     # the dispatch's x reads happen in the layout's time, so the two are
     # rated together: each rate below divides bytes by the time of the
     # kernels that move them.

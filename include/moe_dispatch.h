@@ -269,7 +269,7 @@ int moe_dispatch(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
  * x contiguous) so that the scatter finds them in the 256 MB Infinity Cache
  * instead of interleaving row reads from HBM with its writes.  When every
  * row was read ahead, the bf16 scatter runs with fewer waves in flight (at
- * most 8 workgroups of 64 threads per compute unit), which narrows the
+ * most 7 workgroups of 64 threads per compute unit), which narrows the
  * window of destination rows being written at once.
  *
  *  x, x_stride, bs, hidden                   as for moe_dispatch.

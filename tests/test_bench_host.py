@@ -1,7 +1,8 @@
 """Host logic of bench.py, without a GPU: the algorithmic byte counts
 against the per-configuration totals of the workloads (real rows only,
-metadata once per kernel), the buffer-set rule, the traffic summary's source
-check, the one-GPU rule, and a short CPU-oracle baseline leg."""
+metadata once per kernel), the buffer-set rule, the graph-size rule, the
+traffic summary's source check, the one-GPU rule, and a short CPU-oracle
+baseline leg."""
 
 import importlib.util
 import os
@@ -86,6 +87,15 @@ def test_traffic_needs_the_current_kernel_source(bench, tmp_path, monkeypatch):
     assert bench.read_traffic("decode") is None          # recorded for the skewed line only
     src.write_text("// kernel, changed\n")
     assert bench.read_traffic("skewed") is None
+
+
+@pytest.mark.parametrize("steps,per_graph", [(20, 20), (100, 20), (40, 20), (10, 10), (7, 7),
+                                            (13, 1), (21, 7), (30, 15), (1, 1)])
+def test_graph_size_divides_the_timed_steps(bench, steps, per_graph):
+    """The timed region replays whole graphs of at most GRAPH_STEPS steps."""
+    got = bench.steps_per_graph(steps)
+    assert got == per_graph
+    assert steps % got == 0 and got <= bench.GRAPH_STEPS
 
 
 def test_more_than_one_gpu_is_refused():

@@ -741,7 +741,7 @@ def test_maximum_dimensions():
 
 def test_maximum_row_two_launch_fused():
     """moe_dispatch_fused above 2048 pairs at the largest row (H = 65536,
-    E = 512, K = 16): the layout launches read the 26 MB of rows ahead and the
+    E = 512, K = 16): the layout launch reads the 26 MB of rows ahead and the
     scatter runs in its cache-resident shape (128 chunks of 64 threads per
     row); every element against the oracle."""
     moe = moe_mod()
