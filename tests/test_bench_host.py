@@ -90,7 +90,7 @@ def test_traffic_needs_the_current_kernel_source(bench, tmp_path, monkeypatch):
 
 
 @pytest.mark.parametrize("steps,per_graph", [(20, 20), (100, 20), (40, 20), (10, 10), (7, 7),
-                                            (13, 1), (21, 7), (30, 15), (1, 1)])
+                                            (13, 13), (23, 1), (21, 7), (30, 15), (1, 1)])
 def test_graph_size_divides_the_timed_steps(bench, steps, per_graph):
     """The timed region replays whole graphs of at most GRAPH_STEPS steps."""
     got = bench.steps_per_graph(steps)
