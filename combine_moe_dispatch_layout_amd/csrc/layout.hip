@@ -21,8 +21,11 @@
 //   earlier chunks, turns local ranks into ranks within the workgroup.
 //   Nothing positional is decided by an atomic race, so the layout is
 //   deterministic.
-// Repeated ids: each thread checks one token's K ids against each other in
-//   registers.
+// Repeated ids: when K divides the wave, each 64-pair sub-round holds whole
+//   tokens, so a repeat is a second bit among the token's K lanes in the
+//   expert's mask; otherwise (and for logical repeats under a replica map)
+//   the chunk's ids are staged in LDS and each thread compares one token's
+//   K ids in registers.
 // Single workgroup (<= 2048 pairs): the same kernel also writes the counts and
 //   the padded exclusive scan, so small batches take one launch.
 // Several workgroups: each writes its expert histogram to the workspace,
