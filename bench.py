@@ -550,12 +550,21 @@ def main():
 
     def breakdown_step(b, pairs):
         """One step with every kernel launch taking one of `pairs`; returns
-        the pairs taken, in launch order (the combine last)."""
+        the pairs taken, in launch order (the combine last), and with the
+        layout and dispatch as separate calls the number of launches of the
+        layout call (else None)."""
         moe.moe_time_next_launches(pairs)
-        combine(b, front(b))
+        cut = None
+        if args.fused:
+            lay = front(b)
+        else:
+            lay = layout(b)
+            cut = len(pairs) - moe.moe_time_unused_launches()
+            dispatch(b, lay)
+        combine(b, lay)
         used = len(pairs) - moe.moe_time_unused_launches()
         moe.moe_time_next_launches([])
-        return pairs[:used]
+        return pairs[:used], cut
 
     def new_pairs(n):
         """n (start, stop) timing-event pairs, each recorded once so that the
@@ -567,12 +576,16 @@ def main():
             z.record(stream)
         return pairs
 
-    def split_kernels(taken):
+    def split_kernels(taken, cut):
         """Kernel times (ms) of one step by role: the combine is the last
-        launch, the dispatch the one before it, the layout's one or two
-        launches come first; moe_dispatch_fused's single-launch form is one
+        launch; with separate calls the layout call's launches come first and
+        the dispatch call's (a read-ahead launch, then the scatter) follow;
+        from moe_dispatch_fused, the layout launch then the scatter, or one
         fused kernel."""
         ms = [a.elapsed_time(z) for a, z in taken]
+        if cut is not None:
+            return {"layout": sum(ms[:cut]), "dispatch": sum(ms[cut:-1]), "combine": ms[-1],
+                    "layout_launches": cut, "dispatch_launches": len(ms) - 1 - cut}
         if len(ms) == 2:
             return {"layout+dispatch (fused)": ms[0], "combine": ms[1]}
         return {"layout": sum(ms[:-2]), "dispatch": ms[-2], "combine": ms[-1],
@@ -636,8 +649,9 @@ def main():
     steps_taken = [breakdown_step(bufs[(args.steps + i) % sets], new_pairs(16))
                    for i in range(ROOFLINE_STEPS)]
     torch.cuda.synchronize()
-    per_step = [split_kernels(t) for t in steps_taken]
-    kern_ms = {r: [d[r] for d in per_step] for r in per_step[0] if r != "layout_launches"}
+    per_step = [split_kernels(t, cut) for t, cut in steps_taken]
+    kern_ms = {r: [d[r] for d in per_step] for r in per_step[0]
+               if r not in ("layout_launches", "dispatch_launches")}
     com_ms = kern_ms["combine"]
     mean = lambda v: sum(v) / len(v)
 
@@ -705,6 +719,7 @@ def main():
         "kernel_times": (f"events bound to each launch (kernel start to end) in "
                          f"{ROOFLINE_STEPS} eager steps after the timed region"),
         "layout_launches": per_step[0].get("layout_launches", 0),
+        "dispatch_launches": per_step[0].get("dispatch_launches", 1),
         "kernels_ms": {r: round(mean(v), 4) for r, v in kern_ms.items()},
         "kernels_gbs": {r: round(role_bytes[r] / mean(v) / 1e6, 1) for r, v in kern_ms.items()
                         if r in role_bytes},

@@ -507,6 +507,21 @@ void launch_rank(const LayoutPlan& plan, const int32_t* ids, int32_t k, int32_t 
 
 }  // namespace
 
+namespace {
+
+// The read-ahead workgroups alone, for a scatter with no layout launch before
+// it (moe_dispatch).
+__global__ __launch_bounds__(kLayoutThreads) void read_ahead_kernel(ReadAhead ahead) {
+  read_ahead(ahead, 0, (int32_t)gridDim.x, 0, ahead.vecs);
+}
+
+}  // namespace
+
+hipError_t launch_read_ahead(const ReadAhead& ahead, hipStream_t stream) {
+  launch_kernel(read_ahead_kernel, kReadAheadMaxBlocks, kLayoutThreads, stream, ahead);
+  return hipGetLastError();
+}
+
 hipError_t launch_layout(const int32_t* ids, int32_t k, int32_t num_experts, int32_t align,
                          const LayoutPlan& plan, int32_t* counts, int32_t* send,
                          int32_t* expand_idx, int32_t* status, void* workspace,

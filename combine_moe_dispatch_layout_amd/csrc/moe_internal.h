@@ -360,6 +360,12 @@ LayoutPlan plan_layout(int32_t bs, int32_t k);
 inline bool read_ahead_runs(const LayoutPlan& plan, const ReadAhead& ahead) {
   return plan.blocks > 1 && ahead.vecs > 0 && plan.blocks < kReadAheadMaxBlocks;
 }
+// Contiguous token rows of at least this many bytes (and at most
+// kReadAheadMaxBytes) are read ahead before a separate scatter: below it the
+// extra launch costs more than the scatter gains from cache-resident rows.
+constexpr int64_t kScatterReadAheadMinBytes = int64_t(32) << 20;
+// Reads `ahead` into the Infinity Cache in a launch of its own.
+hipError_t launch_read_ahead(const ReadAhead& ahead, hipStream_t stream);
 size_t layout_workspace_bytes(const LayoutPlan& p, int32_t num_experts);
 LayoutScratch layout_scratch(const LayoutPlan& p, int32_t num_experts, void* workspace);
 

@@ -245,6 +245,12 @@ int moe_dispatch_layout_replicated(const int32_t* expert_ids, int32_t bs, int32_
  *                     Dequantise as e4m3_value * s.
  *  status         in/out int32 [1] or NULL: MOE_FLAG_GUARD is OR-ed in when a
  *                     slot falls outside [0, capacity_rows); never cleared.
+ *
+ * Launches: one scatter; for bf16 output, when x is contiguous (x_stride ==
+ * hidden) and its rows total 32 MB to 128 MB, a launch that reads them into
+ * the 256 MB Infinity Cache goes first, so that the scatter writes from
+ * cache-resident rows instead of interleaving row reads from HBM with its
+ * writes.
  */
 int moe_dispatch(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
                  const int32_t* expert_ids, const int32_t* expand_idx,

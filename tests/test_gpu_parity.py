@@ -277,6 +277,29 @@ def test_dispatch_fp8_every_element(bs, h, e, k):
     np.testing.assert_array_equal(gs.view(np.uint32), rs.view(np.uint32))
 
 
+@pytest.mark.parametrize("bs,h,e,k", [(4096, 4096, 256, 8),   # 32 MiB of rows: read ahead
+                                       (4095, 4096, 256, 8),   # just below: scattered from HBM
+                                       (8192, 7168, 64, 2)])   # 112 MiB of rows, K = 2
+def test_dispatch_with_rows_read_ahead(bs, h, e, k):
+    """moe_dispatch to bf16 on contiguous rows of 32 to 128 MB reads them
+    ahead in a launch of its own, then scatters in its cache-resident shape:
+    the whole buffer against the oracle's, padding untouched; a strided copy
+    of the same rows (no read-ahead) and the e4m3 output (never read ahead)
+    at the same sizes give the oracle's buffers too."""
+    rng = np.random.default_rng(bs + h + k)
+    ids = random_ids(rng, bs, e, k)
+    x = random_bf16(rng, (bs, h))
+    got, ref, gf, rf = run_dispatch_bf16(ids, x, e, 128)
+    np.testing.assert_array_equal(got, ref)
+    assert gf == rf == 0
+    got2, ref2, _, _ = run_dispatch_bf16(ids, x, e, 128, x_stride=h + 64)
+    np.testing.assert_array_equal(got2, ref2)
+    del got, ref, got2, ref2
+    gc, gs, rc, rs = run_dispatch_fp8(ids, x, e, 128)
+    np.testing.assert_array_equal(gc, rc)
+    np.testing.assert_array_equal(gs.view(np.uint32), rs.view(np.uint32))
+
+
 def test_fp8_codes_for_every_bf16_value():
     """Every finite bf16 value v with |v| <= 448 quantised in a block whose
     amax is exactly 448 (scale 1: the code is e4m3(v), ties included) and in
