@@ -82,6 +82,10 @@ def parse():
     p.add_argument("--eager", action="store_true",
                    help="launch the timed steps' kernels from the host instead of replaying "
                         "captured HIP graphs")
+    p.add_argument("--prepared", action="store_true",
+                   help="with --eager: each call of a step made through a prepared call "
+                        "(moe.prepare: arguments checked once per buffer set, then only "
+                        "launched)")
     p.add_argument("--no-ceiling", action="store_true",
                    help="skip the practical-ceiling probe (streaming kernels with the "
                         "dispatch's and combine's read:write mixes)")
@@ -424,6 +428,9 @@ def main():
         print("--ep runs the separate calls and takes no --replicas or --fused",
               file=sys.stderr)
         sys.exit(2)
+    if args.prepared and not args.eager:
+        print("--prepared launches from the host: it needs --eager", file=sys.stderr)
+        sys.exit(2)
     if args.ep:
         args.separate = True
     # moe_dispatch_fused (moe_dispatch_fused_replicated with --replicas) is the
@@ -504,49 +511,74 @@ def main():
     rank_offsets = (torch.empty(args.ep + 1, dtype=torch.int32, device=dev) if args.ep
                     else None)
 
+    # Every library call of a step goes through run(): directly, or, while
+    # `collect` is a list, as a prepared call (--prepared) appended to it.
+    collect = None
+
+    def run(entry, *a, **k):
+        if collect is None:
+            return entry(*a, **k)
+        call = moe.prepare(entry, *a, **k)
+        collect.append(call)
+        return call.result
+
     def layout(b):
         if args.ep:
-            return moe.moe_dispatch_layout_ep(ids, w.experts, args.ep, w.align, out=b["layout"],
-                                              rank_offsets=rank_offsets, workspace=ws)[0]
+            return run(moe.moe_dispatch_layout_ep, ids, w.experts, args.ep, w.align,
+                       out=b["layout"], rank_offsets=rank_offsets, workspace=ws)[0]
         if args.replicas > 0:
-            return moe.moe_dispatch_layout_replicated(
-                ids, w.experts, rep_off, rep_thr, 1234, w.align, out=b["layout"],
-                replica_ids=rep_ids, workspace=ws)[1]
-        return moe.moe_dispatch_layout(ids, w.experts, w.align, out=b["layout"], workspace=ws)
+            return run(moe.moe_dispatch_layout_replicated,
+                       ids, w.experts, rep_off, rep_thr, 1234, w.align, out=b["layout"],
+                       replica_ids=rep_ids, workspace=ws)[1]
+        return run(moe.moe_dispatch_layout, ids, w.experts, w.align, out=b["layout"],
+                   workspace=ws)
 
     def dispatch(b, lay):
-        moe.moe_dispatch(b["x"], route_ids, lay.expand_idx, lay.ep_send_counts, n_phys,
-                         expand_x=b["expand_x"], capacity_rows=cap,
-                         out_dtype="fp8" if w.fp8 else "bf16", quant_scales=b["scales"])
+        run(moe.moe_dispatch, b["x"], route_ids, lay.expand_idx, lay.ep_send_counts, n_phys,
+            expand_x=b["expand_x"], capacity_rows=cap, out_dtype="fp8" if w.fp8 else "bf16",
+            quant_scales=b["scales"])
 
     def combine(b, lay):
         if fp8_combine:
-            moe.moe_combine_fp8(b["y_codes"], b["y_scales"], route_ids, lay.expand_idx,
-                                lay.ep_send_counts, scales, b["shared"], n_phys, out=b["out"])
+            run(moe.moe_combine_fp8, b["y_codes"], b["y_scales"], route_ids, lay.expand_idx,
+                lay.ep_send_counts, scales, b["shared"], n_phys, out=b["out"])
         else:
-            moe.moe_combine(b["y"], route_ids, lay.expand_idx, lay.ep_send_counts, scales,
-                            b["shared"], n_phys, out=b["out"])
+            run(moe.moe_combine, b["y"], route_ids, lay.expand_idx, lay.ep_send_counts, scales,
+                b["shared"], n_phys, out=b["out"])
 
     def front(b):
         """Layout and dispatch of one step; returns the layout."""
         if args.fused and args.replicas > 0:
-            moe.moe_dispatch_fused_replicated(
+            run(moe.moe_dispatch_fused_replicated,
                 b["x"], ids, w.experts, rep_off, rep_thr, 1234, w.align, out=b["layout"],
                 replica_ids=rep_ids, capacity_rows=cap, expand_x=b["expand_x"],
                 out_dtype="fp8" if w.fp8 else "bf16", quant_scales=b["scales"], workspace=ws)
             return b["layout"]
         if args.fused:
-            moe.moe_dispatch_fused(b["x"], ids, n_phys, w.align, out=b["layout"],
-                                   capacity_rows=cap, expand_x=b["expand_x"],
-                                   out_dtype="fp8" if w.fp8 else "bf16",
-                                   quant_scales=b["scales"], workspace=ws)
+            run(moe.moe_dispatch_fused, b["x"], ids, n_phys, w.align, out=b["layout"],
+                capacity_rows=cap, expand_x=b["expand_x"], out_dtype="fp8" if w.fp8 else "bf16",
+                quant_scales=b["scales"], workspace=ws)
             return b["layout"]
         lay = layout(b)
         dispatch(b, lay)
         return lay
 
     def step(b):
+        if plans is not None:
+            for call in plans[b["index"]]:
+                call()
+            return
         combine(b, front(b))
+
+    plans = None
+    if args.prepared:
+        # One prepared call per library call of a step, per buffer set.
+        plans = []
+        for b in bufs:
+            collect = []
+            combine(b, front(b))
+            plans.append(collect)
+        collect = None
 
     def breakdown_step(b, pairs):
         """One step with every kernel launch taking one of `pairs`; returns
@@ -706,7 +738,8 @@ def main():
                                                            if w.routing == "zipf" else ""),
                    "align": w.align, "capacity_rows": cap, "buffer_sets": sets,
                    "x_bytes_between_reuse": 2 * w.bs * w.hidden * (sets - 1),
-                   "launch": ("eager" if args.eager else f"hip graphs of {per_graph} steps"),
+                   "launch": (("eager, prepared calls" if args.prepared else "eager")
+                              if args.eager else f"hip graphs of {per_graph} steps"),
                    "layout_dispatch": (("moe_dispatch_fused_replicated" if args.replicas > 0
                                         else "moe_dispatch_fused") if args.fused
                                        else "separate"),

@@ -42,12 +42,16 @@ Entry points (same names as the C ABI):
 * ``moe_time_next_launches(pairs)`` / ``moe_time_unused_launches()``
   (measurement only: torch events stamped with the next kernels' own start
   and end)
+* ``prepare(entry, *args, **kwargs)`` -> ``Prepared``: an entry point's call
+  checked once, for loops that repeat it on the same tensors (a call then
+  only launches)
 """
 
 from __future__ import annotations
 
 import ctypes
 import os
+import threading
 
 import numpy as np
 from typing import NamedTuple, Optional
@@ -62,7 +66,7 @@ __all__ = [
     "moe_dispatch_fused_noalloc", "moe_noalloc_scratch_bytes",
     "moe_plan_compensation",
     "moe_combine_fp8", "moe_probe_stream_mix", "moe_probe_empty", "moe_time_next_launches",
-    "moe_time_unused_launches",
+    "moe_time_unused_launches", "prepare", "Prepared",
     "MOE_BF16", "MOE_FP8_E4M3", "MOE_FLAG_ID_RANGE", "MOE_FLAG_DUP_ID", "MOE_FLAG_GUARD",
 ]
 
@@ -141,6 +145,65 @@ def load_library() -> ctypes.CDLL:
 def _check(rc: int) -> None:
     if rc != MOE_OK:
         raise MoeError(rc, load_library().moe_status_string(rc).decode())
+
+
+# While prepare() runs an entry point, its library launch is recorded here
+# (per host thread) instead of being made.
+_recording = threading.local()
+
+
+def _launch(fn, *args) -> int:
+    calls = getattr(_recording, "calls", None)
+    if calls is not None:
+        calls.append((fn, args))
+        return MOE_OK
+    return fn(*args)
+
+
+class Prepared:
+    """A library call validated once: calling it repeats the same launch
+    (same tensors, same stream) with no argument checks, for tight serving
+    loops launched from the host.  ``result`` holds what the entry point
+    returned (its output tensors, which every call overwrites)."""
+
+    def __init__(self, name: str, fn, args, result):
+        self.name = name
+        self.result = result
+        self._fn = fn
+        self._args = args
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != MOE_OK:
+            _check(rc)
+        return self.result
+
+
+def prepare(entry, *args, **kwargs) -> Prepared:
+    """Run entry point ``entry`` (e.g. ``moe_dispatch_fused``) with these
+    arguments through all of its checks and output allocation, but instead of
+    launching, return a Prepared call that launches it.  The tensors it was
+    given or allocated must stay alive and keep their shapes, strides and
+    devices; their contents may change between calls.  The launch goes to
+    the stream that was current when prepare() ran.  ``check=True`` cannot
+    be prepared (it synchronises)."""
+    if kwargs.get("check"):
+        raise ValueError("check=True cannot be prepared")
+    _recording.calls = []
+    try:
+        result = entry(*args, **kwargs)
+        calls = _recording.calls
+    finally:
+        _recording.calls = None
+    if len(calls) != 1:
+        raise ValueError(f"{getattr(entry, '__name__', entry)} does not make one library launch")
+    fn, raw = calls[0]
+    # Arguments converted once to the C types the function declares, so a
+    # call skips the per-argument conversion.
+    types = getattr(fn, "argtypes", None)
+    conv = raw if types is None else tuple(
+        a if a is None or isinstance(a, t) else t(a) for t, a in zip(types, raw))
+    return Prepared(getattr(entry, "__name__", str(entry)), fn, conv, result)
 
 
 class MoeStatusError(MoeError):
@@ -375,7 +438,7 @@ def moe_dispatch_layout(expert_ids: torch.Tensor, num_experts: int, align: int =
     dev = expert_ids.get_device()
     out = _layout(out, num_experts, bs * k, dev)
     workspace = _workspace(workspace, bs, k, num_experts, dev)
-    rc = load_library().moe_dispatch_layout(
+    rc = _launch(load_library().moe_dispatch_layout,
         _ptr(expert_ids), bs, k, num_experts, align, _ptr(out.expert_counts),
         _ptr(out.ep_send_counts), _ptr(out.expand_idx), _ptr(out.status), _ptr(workspace),
         _nbytes(workspace), _stream(expert_ids))
@@ -426,7 +489,7 @@ def moe_dispatch(x: torch.Tensor, expert_ids: torch.Tensor, expand_idx: torch.Te
     capacity_rows, expand_x, quant_scales = _scatter_outputs(
         expand_x, quant_scales, capacity_rows, bs, k, hidden, num_experts, align, dtype, dev)
     status = _status_word(status, check, dev)
-    rc = load_library().moe_dispatch(
+    rc = _launch(load_library().moe_dispatch,
         _ptr(x), _row_stride(x, "x"), bs, hidden, _ptr(expert_ids), _ptr(expand_idx),
         _ptr(ep_send_counts), k, num_experts, _ptr(expand_x), _row_stride(expand_x, "expand_x"),
         capacity_rows, dtype, _ptr(quant_scales) if dtype == MOE_FP8_E4M3 else None,
@@ -457,7 +520,7 @@ def moe_dispatch_fused(x: torch.Tensor, expert_ids: torch.Tensor, num_experts: i
     capacity_rows, expand_x, quant_scales = _scatter_outputs(
         expand_x, quant_scales, capacity_rows, bs, k, hidden, num_experts, align, dtype, dev)
     workspace = _workspace(workspace, bs, k, num_experts, dev)
-    rc = load_library().moe_dispatch_fused(
+    rc = _launch(load_library().moe_dispatch_fused,
         _ptr(x), _row_stride(x, "x"), bs, hidden, _ptr(expert_ids), k, num_experts, align,
         _ptr(out.expert_counts), _ptr(out.ep_send_counts), _ptr(out.expand_idx),
         _ptr(expand_x), _row_stride(expand_x, "expand_x"), capacity_rows, dtype,
@@ -489,7 +552,7 @@ def moe_dispatch_fused_noalloc(x: torch.Tensor, expert_ids: torch.Tensor, num_ex
     out = _layout(out, num_experts, bs * k, dev)
     capacity_rows, expand_x, quant_scales = _scatter_outputs(
         expand_x, quant_scales, capacity_rows, bs, k, hidden, num_experts, align, dtype, dev)
-    rc = load_library().moe_dispatch_fused_noalloc(
+    rc = _launch(load_library().moe_dispatch_fused_noalloc,
         _ptr(x), _row_stride(x, "x"), bs, hidden, _ptr(expert_ids), k, num_experts, align,
         _ptr(out.expert_counts), _ptr(out.ep_send_counts), _ptr(out.expand_idx),
         _ptr(expand_x), _row_stride(expand_x, "expand_x"), capacity_rows, dtype,
@@ -537,7 +600,7 @@ def moe_combine(expand_x: torch.Tensor, expert_ids: torch.Tensor, expand_idx: to
     cap, hidden = expand_x.shape
     shared_stride, out = _combine_rows(shared_expert_x, out, bs, hidden, dev)
     status = _status_word(status, check, dev)
-    rc = load_library().moe_combine(
+    rc = _launch(load_library().moe_combine,
         _ptr(expand_x), ys, cap, _ptr(expert_ids), _ptr(expand_idx), _ptr(ep_send_counts),
         _ptr(expert_scales), _ptr(shared_expert_x), shared_stride, bs, hidden, k, num_experts,
         _ptr(out), _ptr(status), _stream(expand_x))
@@ -568,7 +631,7 @@ def moe_combine_fp8(expand_x: torch.Tensor, quant_scales: torch.Tensor, expert_i
         raise ValueError("quant_scales must be [capacity_rows, hidden/128]")
     shared_stride, out = _combine_rows(shared_expert_x, out, bs, hidden, dev)
     status = _status_word(status, check, dev)
-    rc = load_library().moe_combine_fp8(
+    rc = _launch(load_library().moe_combine_fp8,
         _ptr(expand_x), ys, cap, _ptr(quant_scales), _ptr(expert_ids), _ptr(expand_idx),
         _ptr(ep_send_counts), _ptr(expert_scales), _ptr(shared_expert_x), shared_stride, bs,
         hidden, k, num_experts, _ptr(out), _ptr(status), _stream(expand_x))
@@ -609,7 +672,7 @@ def moe_dispatch_layout_replicated(expert_ids: torch.Tensor, num_experts: int,
     out = _layout(out, p, bs * k, dev)
     replica_ids = _replica_ids(replica_ids, bs, k, dev)
     workspace = _workspace(workspace, bs, k, p, dev)
-    rc = load_library().moe_dispatch_layout_replicated(
+    rc = _launch(load_library().moe_dispatch_layout_replicated,
         _ptr(expert_ids), bs, k, num_experts, _ptr(replica_offsets), _ptr(replica_thresholds), p,
         seed & 0xFFFFFFFFFFFFFFFF, align, _ptr(replica_ids), _ptr(out.expert_counts),
         _ptr(out.ep_send_counts), _ptr(out.expand_idx), _ptr(out.status), _ptr(workspace),
@@ -645,7 +708,7 @@ def moe_dispatch_fused_replicated(x: torch.Tensor, expert_ids: torch.Tensor, num
     capacity_rows, expand_x, quant_scales = _scatter_outputs(
         expand_x, quant_scales, capacity_rows, bs, k, hidden, p, align, dtype, dev)
     workspace = _workspace(workspace, bs, k, p, dev)
-    rc = load_library().moe_dispatch_fused_replicated(
+    rc = _launch(load_library().moe_dispatch_fused_replicated,
         _ptr(x), _row_stride(x, "x"), bs, hidden, _ptr(expert_ids), k, num_experts,
         _ptr(replica_offsets), _ptr(replica_thresholds), p, seed & 0xFFFFFFFFFFFFFFFF, align,
         _ptr(replica_ids), _ptr(out.expert_counts), _ptr(out.ep_send_counts),
@@ -675,7 +738,7 @@ def moe_dispatch_layout_ep(expert_ids: torch.Tensor, num_experts: int, ep_world_
     _need(rank_offsets, torch.int32, "rank_offsets", device=dev)
     _need_len(rank_offsets, max(ep_world_size, 0) + 1, "rank_offsets")
     workspace = _workspace(workspace, bs, k, num_experts, dev)
-    rc = load_library().moe_dispatch_layout_ep(
+    rc = _launch(load_library().moe_dispatch_layout_ep,
         _ptr(expert_ids), bs, k, num_experts, ep_world_size, align, _ptr(out.expert_counts),
         _ptr(out.ep_send_counts), _ptr(rank_offsets), _ptr(out.expand_idx), _ptr(out.status),
         _ptr(workspace), _nbytes(workspace), _stream(expert_ids))

@@ -106,7 +106,7 @@ def test_more_than_one_gpu_is_refused():
 
 
 @pytest.mark.parametrize("flags", [["--fused", "--separate"], ["--ep", "8", "--replicas", "4"],
-                                   ["--ep", "8", "--fused"]])
+                                   ["--ep", "8", "--fused"], ["--prepared"]])
 def test_conflicting_options_are_refused(flags):
     """Refused before anything touches a GPU."""
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *flags],

@@ -264,3 +264,25 @@ def test_check_is_off_by_default(stub):
     moe.moe_dispatch(**dispatch_args(), status=i32(1))
     moe.moe_dispatch_fused(bf16(BS, H), i32(BS, K), E)
     assert stub.calls == ["moe_dispatch", "moe_dispatch_fused"]
+
+
+def test_prepare_records_one_launch_and_repeats_it(stub):
+    """prepare() runs every check and allocates the outputs once, records the
+    entry point's one library launch instead of making it, and each call of
+    the result makes exactly that launch again."""
+    x, ids = bf16(BS, H), i32(BS, K)
+    call = moe.prepare(moe.moe_dispatch_fused, x, ids, E, workspace=torch.zeros(WS_BYTES,
+                                                                                  dtype=torch.uint8))
+    assert stub.calls == []
+    lay, ex = call.result
+    assert ex.shape == (oracle.capacity(BS, K, E, 128), H)
+    for n in range(1, 4):
+        assert call() is call.result
+        assert stub.calls == ["moe_dispatch_fused"] * n
+    with pytest.raises(ValueError):
+        moe.prepare(moe.moe_dispatch_fused, x, i32(BS - 1, K), E)   # the checks still run
+    with pytest.raises(ValueError):
+        moe.prepare(moe.moe_dispatch_layout, ids, E, check=True)     # synchronises: refused
+    with pytest.raises(ValueError):
+        moe.prepare(moe.moe_dispatch_capacity, BS, K, E)             # launches nothing
+    assert stub.calls == ["moe_dispatch_fused"] * 3
