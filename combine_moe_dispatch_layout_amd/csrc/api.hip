@@ -85,10 +85,10 @@ int scatter_args_check(const void* x, int64_t x_stride, int32_t hidden, const vo
 // expert_ids, or the replica ids it writes), on one stream.  With several
 // ranking workgroups this is two launches: the ranking launch, whose last
 // workgroup also scans the histograms and whose spare workgroups read
-// contiguous token rows ahead (at most kReadAheadMaxBytes), and the
-// scatter, which adds each token's workgroup prefix to its ranks and writes
-// expand_idx.  When every row was read ahead, the bf16 scatter takes its
-// cache-resident launch shape.
+// contiguous token rows ahead (all of them up to kReadAheadMaxBytes, else
+// the first kReadAheadPartBytes), and the scatter, which adds each token's
+// workgroup prefix to its ranks and writes expand_idx.  When every row was
+// read ahead, the bf16 scatter takes its cache-resident launch shape.
 int layout_then_scatter(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
                         const int32_t* expert_ids, const int32_t* route_ids, int32_t k,
                         int32_t ranked, int32_t align, const moe::LayoutPlan& plan,
@@ -103,9 +103,8 @@ int layout_then_scatter(const void* x, int64_t x_stride, int32_t bs, int32_t hid
   bool rows_cached = false;  // every token row read ahead
   if (bs > 0 && x_stride == hidden) {
     const int64_t vecs = (int64_t)bs * hidden / 8;
-    const int64_t max_vecs = moe::kReadAheadMaxBytes / 16;
     ahead.base = static_cast<const moe::u32x4*>(x);
-    ahead.vecs = vecs < max_vecs ? vecs : max_vecs;
+    ahead.vecs = vecs <= moe::kReadAheadMaxBytes / 16 ? vecs : moe::kReadAheadPartBytes / 16;
     rows_cached = ahead.vecs == vecs && moe::read_ahead_runs(plan, ahead);
   }
   // With several ranking workgroups the ranks are left to the scatter (no

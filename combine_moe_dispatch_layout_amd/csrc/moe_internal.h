@@ -286,8 +286,12 @@ struct RankSplit {
 // workgroups (together with the ranking workgroups) read the rows the
 // scatter will need with ordinary loads, which allocate in the 256 MB
 // Infinity Cache; the scatter then finds them there instead of mixing row
-// reads from HBM into its write stream.  At most kReadAheadMaxBytes are read
-// ahead (half the cache).
+// reads from HBM into its write stream.  Token rows of up to
+// kReadAheadMaxBytes are read ahead whole; of larger x only the first
+// kReadAheadPartBytes, because a partial read-ahead leaves the scatter
+// reading the rest from HBM, and a longer one than that was measured slower
+// (192 MB of the 235 MB of the 16384-token line: 800 against 794 us per
+// step, where reading all 235 MB ahead took 780 us).
 struct ReadAhead {
   const u32x4* base = nullptr;
   int64_t vecs = 0;   // 16-byte vectors, from base
@@ -305,7 +309,8 @@ constexpr int64_t kSerialMinItems = 8192;
 #define MOE_READ_AHEAD_BLOCKS 240  // of the 256 compute units, with the ranking workgroups
 #endif
 constexpr int kReadAheadMaxBlocks = MOE_READ_AHEAD_BLOCKS;
-constexpr int64_t kReadAheadMaxBytes = int64_t(128) << 20;
+constexpr int64_t kReadAheadMaxBytes = int64_t(240) << 20;   // of the 256 MB Infinity Cache
+constexpr int64_t kReadAheadPartBytes = int64_t(128) << 20;
 // Loads in flight per read-ahead thread: enough to keep HBM busy, few enough
 // that the ranking workgroups' own loads in the same launch do not queue
 // behind a deep backlog.

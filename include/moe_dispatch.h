@@ -247,7 +247,7 @@ int moe_dispatch_layout_replicated(const int32_t* expert_ids, int32_t bs, int32_
  *                     slot falls outside [0, capacity_rows); never cleared.
  *
  * Launches: one scatter; for bf16 output, when x is contiguous (x_stride ==
- * hidden) and its rows total 32 MB to 128 MB, a launch that reads them into
+ * hidden) and its rows total 32 MB to 240 MB, a launch that reads them into
  * the 256 MB Infinity Cache goes first, so that the scatter writes from
  * cache-resident rows instead of interleaving row reads from HBM with its
  * writes.
@@ -271,12 +271,13 @@ int moe_dispatch(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
  * histograms, as in moe_dispatch_layout), then the scatter, which adds each
  * token's workgroup prefix to the ranks and writes expand_idx itself, so no
  * finalize launch sits between them.  The ranking launch, which is latency
- * bound, also reads the token rows x ahead (ordinary loads, at most 128 MB,
- * x contiguous) so that the scatter finds them in the 256 MB Infinity Cache
- * instead of interleaving row reads from HBM with its writes.  When every
- * row was read ahead, the bf16 scatter runs with fewer waves in flight (at
- * most 7 workgroups of 64 threads per compute unit), which narrows the
- * window of destination rows being written at once.
+ * bound, also reads the token rows x ahead (ordinary loads, x contiguous:
+ * all rows up to 240 MB, else the first 128 MB) so that the scatter finds
+ * them in the 256 MB Infinity Cache instead of interleaving row reads from
+ * HBM with its writes.  When every row was read ahead, the bf16 scatter
+ * runs with fewer waves in flight (at most 7 workgroups of 64 threads per
+ * compute unit), which narrows the window of destination rows being
+ * written at once.
  *
  *  x, x_stride, bs, hidden                   as for moe_dispatch.
  *  expert_ids, k, num_experts, align         as for moe_dispatch_layout.
@@ -386,10 +387,10 @@ int moe_combine_fp8(const void* expand_x, int64_t expand_x_stride, int64_t capac
  * padding rows left unwritten, e4m3 codes and scales, status bits).  As in
  * moe_dispatch_fused, batches of more than 2048 pairs take the ranking
  * launch, which also reads the token rows ahead into the Infinity Cache (x
- * contiguous, at most 128 MB), and the scatter, which completes expand_idx;
- * a bf16 scatter of rows that were all read ahead runs with fewer waves in
- * flight.  Batches of at most 2048 pairs take one layout launch and the
- * scatter launch.
+ * contiguous; all rows up to 240 MB, else the first 128 MB), and the
+ * scatter, which completes expand_idx; a bf16 scatter of rows that were all
+ * read ahead runs with fewer waves in flight.  Batches of at most 2048
+ * pairs take one layout launch and the scatter launch.
  *
  *  x, x_stride, hidden, expand_x, expand_x_stride, capacity_rows, out_dtype,
  *  quant_scales               as for moe_dispatch (over num_replicas).

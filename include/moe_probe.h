@@ -62,7 +62,7 @@ int moe_probe_stream_mix(const void* src, int64_t src_rows_total, void* dst,
  * An entry point makes one launch per kernel: moe_dispatch_layout one or two
  * (one when a single workgroup ranks the batch); moe_dispatch one, or two (a
  * read-ahead of the token rows, then the scatter) for bf16 output from
- * contiguous rows of 32 to 128 MB; moe_dispatch_fused one (fused kernel, bs*k <= 2048) or two (the
+ * contiguous rows of 32 to 240 MB; moe_dispatch_fused one (fused kernel, bs*k <= 2048) or two (the
  * layout's ranking launch, then the scatter); moe_combine and
  * moe_combine_fp8 one.  Calls that return an error or have nothing to do
  * launch nothing and leave the pairs bound.

@@ -174,6 +174,19 @@ def test_two_launch_path_matches_the_oracle(bs, h, e, k, align):
     assert check_against_oracle(ids, random_bf16(rng, (bs, h)), e, align) == 0
 
 
+@pytest.mark.parametrize("bs", [17554,    # 240 MiB of rows less 4 KB: every row read ahead
+                                17555])   # just over: the first 128 MiB read ahead, the
+                                          # scatter in its shape for rows from HBM
+def test_two_launch_path_at_the_read_ahead_limit(bs):
+    """The ranking launch reads all of x ahead up to 240 MiB and only the
+    first 128 MiB of a larger x; on both sides of that limit the whole
+    buffer equals the oracle's."""
+    rng = np.random.default_rng(bs)
+    h, e, k = 7168, 64, 2
+    ids = random_ids(rng, bs, e, k)
+    assert check_against_oracle(ids, random_bf16(rng, (bs, h)), e, 128) == 0
+
+
 def test_two_launch_path_guard_and_hot_experts():
     rng = np.random.default_rng(9)
     bs, h, e, k = 700, 256, 16, 8

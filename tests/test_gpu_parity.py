@@ -279,9 +279,11 @@ def test_dispatch_fp8_every_element(bs, h, e, k):
 
 @pytest.mark.parametrize("bs,h,e,k", [(4096, 4096, 256, 8),   # 32 MiB of rows: read ahead
                                        (4095, 4096, 256, 8),   # just below: scattered from HBM
-                                       (8192, 7168, 64, 2)])   # 112 MiB of rows, K = 2
+                                       (8192, 7168, 64, 2),    # 112 MiB of rows, K = 2
+                                       (17554, 7168, 64, 2),   # just under 240 MiB: read ahead
+                                       (17555, 7168, 64, 2)])  # just over: scattered from HBM
 def test_dispatch_with_rows_read_ahead(bs, h, e, k):
-    """moe_dispatch to bf16 on contiguous rows of 32 to 128 MB reads them
+    """moe_dispatch to bf16 on contiguous rows of 32 to 240 MB reads them
     ahead in a launch of its own, then scatters in its cache-resident shape:
     the whole buffer against the oracle's, padding untouched; a strided copy
     of the same rows (no read-ahead) and the e4m3 output (never read ahead)
