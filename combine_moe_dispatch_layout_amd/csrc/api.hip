@@ -66,7 +66,9 @@ struct TimedLaunches {
 };
 thread_local TimedLaunches tl_timed;
 
-// Row and scale rules of the scatter's inputs and outputs (bs > 0).
+// Row and scale rules of the scatter's inputs and outputs (bs > 0).  With no
+// capacity nothing is written (every pair is guarded), so the output buffers
+// may then be absent.
 int scatter_args_check(const void* x, int64_t x_stride, int32_t hidden, const void* expand_x,
                        int64_t expand_x_stride, int64_t capacity_rows, int32_t out_dtype,
                        const float* quant_scales) {
@@ -258,15 +260,9 @@ int moe_dispatch(const void* x, int64_t x_stride, int32_t bs, int32_t hidden,
   if (bs == 0) return MOE_OK;
   if (expert_ids == nullptr || expand_idx == nullptr || ep_send_counts == nullptr)
     return MOE_ERR_INVALID_ARG;
-  if (!row_ok(x, x_stride, hidden, 2)) return MOE_ERR_INVALID_ARG;
-  // With no capacity nothing is written (every pair is guarded), so the
-  // output buffers may be absent.
-  const int out_elem = out_dtype == MOE_BF16 ? 2 : 1;
-  if (capacity_rows > 0 && !row_ok(expand_x, expand_x_stride, hidden, out_elem))
-    return MOE_ERR_INVALID_ARG;
-  if (out_dtype == MOE_FP8_E4M3 && capacity_rows > 0 &&
-      (quant_scales == nullptr || (reinterpret_cast<uintptr_t>(quant_scales) & 3u) != 0))
-    return MOE_ERR_INVALID_ARG;
+  const int err = scatter_args_check(x, x_stride, hidden, expand_x, expand_x_stride,
+                                     capacity_rows, out_dtype, quant_scales);
+  if (err != MOE_OK) return err;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // Contiguous rows of a bandwidth-bound bf16 batch are read ahead first, so
   // that the scatter writes from cache-resident rows instead of interleaving
