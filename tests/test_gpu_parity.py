@@ -764,6 +764,71 @@ def test_maximum_dimensions():
     np.testing.assert_array_equal(host_bits(ex), oracle.dispatch_bf16(x, ids, r, s, e, cap)[0])
 
 
+def test_token_rows_beyond_2gib():
+    """150,000 tokens of H = 7168: x, the shared rows and the combine's
+    output are 2.15 GB each, so the last tokens' offsets pass 2^31 bytes.
+    Through moe_dispatch_fused (bf16: the first 128 MB read ahead and the
+    scatter's shape for rows from HBM; e4m3) and moe_combine (identity
+    experts, unit weights, x as the shared rows): the layout and the whole
+    bf16 buffer against the oracle, and the e4m3 rows and combined tokens
+    of the first 1000 and the last 3000 tokens (the oracle's e4m3 and
+    combine passes over all 150,000 take most of a minute).  Every row
+    carries its token index in two channels (normal bf16 values), so a
+    truncated offset reads a row that differs."""
+    moe = moe_mod()
+    rng = np.random.default_rng(31)
+    bs, h, e, k, align = 150_000, 7168, 8, 1, 128
+    assert (bs - 3000) * h * 2 < 2**31 < bs * h * 2
+    x = np.tile(random_bf16(rng, (4096, h)), ((bs + 4095) // 4096, 1))[:bs]
+    tok = np.arange(bs, dtype=np.uint32)
+    x[:, 0] = (0x2000 | (tok & 0x1FFF)).astype(np.uint16)
+    x[:, 1] = (0x2000 | ((tok >> 13) & 0x1FFF)).astype(np.uint16)
+    ids = random_ids(rng, bs, e, k)
+    c, s, r, f = oracle.layout(ids, e, align)
+    assert f == 0
+    cap = oracle.capacity(bs, k, e, align)
+    xd, idd = bf16_dev(x), dev(ids)
+    sentinel = int(np.uint16(oracle.SENTINEL_BF16).view(np.int16))
+    sub = np.concatenate([np.arange(1000), np.arange(bs - 3000, bs)])
+    sub_slots = (s[ids[sub]] + r.reshape(bs, k)[sub]).reshape(-1)
+
+    ex = torch.full((cap, h), sentinel, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    lay, _ = moe.moe_dispatch_fused(xd, idd, e, align, expand_x=ex, capacity_rows=cap)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(lay.expert_counts.cpu().numpy(), c)
+    np.testing.assert_array_equal(lay.ep_send_counts.cpu().numpy(), s)
+    np.testing.assert_array_equal(lay.expand_idx.cpu().numpy(), r)
+    assert int(lay.status.cpu()[0]) == 0
+    y = host_bits(ex)
+    ref, rf = oracle.dispatch_bf16(x, ids, r, s, e, cap)
+    assert rf == 0
+    np.testing.assert_array_equal(y, ref)
+    del ref
+
+    sc = np.ones((bs, k), np.float32)
+    out = moe.moe_combine(ex, idd, lay.expand_idx, lay.ep_send_counts, dev(sc), xd, e)
+    torch.cuda.synchronize()
+    got = out[torch.from_numpy(sub).to(DEV)]
+    ref, rf = oracle.combine(y, ids[sub], r.reshape(bs, k)[sub].reshape(-1), s, sc[sub],
+                             x[sub], e)
+    assert rf == 0
+    np.testing.assert_array_equal(host_bits(got), ref)
+    del out, got, ref, y, ex
+
+    codes = torch.full((cap, h), oracle.SENTINEL_FP8, dtype=torch.uint8, device=DEV)
+    qs = torch.full((cap, h // 128), oracle.SENTINEL_SCALE, dtype=torch.float32, device=DEV)
+    moe.moe_dispatch_fused(xd, idd, e, align, capacity_rows=cap, out_dtype="fp8",
+                           expand_x=codes, quant_scales=qs)
+    torch.cuda.synchronize()
+    rc, rs, rf = oracle.dispatch_fp8(x[sub], ids[sub], r.reshape(bs, k)[sub].reshape(-1), s, e,
+                                     cap)
+    assert rf == 0
+    rows = torch.from_numpy(sub_slots).to(DEV)
+    np.testing.assert_array_equal(codes[rows].cpu().numpy(), rc[sub_slots])
+    np.testing.assert_array_equal(qs[rows].cpu().numpy().view(np.uint32),
+                                  rs[sub_slots].view(np.uint32))
+
+
 def test_maximum_row_two_launch_fused():
     """moe_dispatch_fused above 2048 pairs at the largest row (H = 65536,
     E = 512, K = 16): the layout launch reads the 26 MB of rows ahead and the
