@@ -118,85 +118,163 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t i) {
   return z ^ (z >> 31);
 }
 
+// Loads / stores W adjacent histogram columns (W = 4: one 16-byte access).
+template <int W>
+__device__ __forceinline__ void load_cols(const int32_t* p, int (&v)[W]) {
+  if constexpr (W == 4) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v[w] = (int)q[w];
+  } else {
+    v[0] = *p;
+  }
+}
+template <int W>
+__device__ __forceinline__ void store_cols(int32_t* p, const int (&v)[W]) {
+  if constexpr (W == 4) {
+    *reinterpret_cast<u32x4*>(p) = u32x4{(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2],
+                                         (uint32_t)v[3]};
+  } else {
+    *p = v[0];
+  }
+}
+
+// Each expert's column of the workgroup histograms ws.hist[b*E + e] is
+// scanned once, in place, into the exclusive prefix over workgroups
+// (workgroup b's first rank for that expert); totals[e] receives the column
+// sum, the expert's count.  Threads own W adjacent columns (W = 4 when E is a
+// multiple of 4, so every access is 16 bytes) and a run of rows, loaded in
+// batches of kScanBatch accesses in flight.  A run of at most kScanKeep rows
+// stays in registers between the two passes; a longer one is read again in
+// the second pass.  `part` is LDS scratch of W * kLayoutThreads ints.
+constexpr int kScanBatch = 16;
+template <int W>
+__device__ __forceinline__ void scan_columns(const LayoutScratch& ws, int32_t blocks, int32_t E,
+                                             int* part, int* totals) {
+  constexpr int kScanKeep = 16 / W;
+  const int tid = threadIdx.x;
+  const int ncol = E / W;
+  int cpad = 1;
+  while (cpad < ncol) cpad <<= 1;
+  const int groups = kLayoutThreads / cpad;  // threads per column group, each a run of rows
+  const int col = tid & (cpad - 1);
+  const int grp = tid / cpad;
+  const int rows = (blocks + groups - 1) / groups;
+  const int r0 = min(blocks, grp * rows), r1 = min(blocks, r0 + rows);
+  const bool active = col < ncol;
+  const bool keep = r1 - r0 <= kScanKeep;
+  int32_t* __restrict__ h = ws.hist + col * W;
+
+  // Pass 1: this thread's partial column sums.
+  int partial[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) partial[w] = 0;
+  int kept[kScanKeep][W];
+  if (active && keep) {
+#pragma unroll
+    for (int u = 0; u < kScanKeep; ++u) {
+      if (r0 + u < r1) {
+        load_cols<W>(h + (int64_t)(r0 + u) * E, kept[u]);
+      } else {
+#pragma unroll
+        for (int w = 0; w < W; ++w) kept[u][w] = 0;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kScanKeep; ++u)
+#pragma unroll
+      for (int w = 0; w < W; ++w) partial[w] += kept[u][w];
+  } else if (active) {
+    for (int b0 = r0; b0 < r1; b0 += kScanBatch) {
+      int v[kScanBatch][W];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) {
+        if (b0 + u < r1) {
+          load_cols<W>(h + (int64_t)(b0 + u) * E, v[u]);
+        } else {
+#pragma unroll
+          for (int w = 0; w < W; ++w) v[u][w] = 0;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u)
+#pragma unroll
+        for (int w = 0; w < W; ++w) partial[w] += v[u][w];
+    }
+  }
+#pragma unroll
+  for (int w = 0; w < W; ++w) part[w * kLayoutThreads + tid] = partial[w];
+  __syncthreads();
+  int run[W], total[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    run[w] = 0;
+    total[w] = 0;
+    for (int g = 0; g < groups; ++g) {
+      const int p = part[w * kLayoutThreads + g * cpad + col];
+      run[w] += (g < grp) ? p : 0;
+      total[w] += p;
+    }
+  }
+  // Pass 2: the exclusive prefix down the columns, written over the counts.
+  if (active && keep) {
+#pragma unroll
+    for (int u = 0; u < kScanKeep; ++u) {
+      if (r0 + u < r1) {
+        store_cols<W>(h + (int64_t)(r0 + u) * E, run);
+#pragma unroll
+        for (int w = 0; w < W; ++w) run[w] += kept[u][w];
+      }
+    }
+  } else if (active) {
+    for (int b0 = r0; b0 < r1; b0 += kScanBatch) {
+      int v[kScanBatch][W];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) {
+        if (b0 + u < r1) {
+          load_cols<W>(h + (int64_t)(b0 + u) * E, v[u]);
+        } else {
+#pragma unroll
+          for (int w = 0; w < W; ++w) v[u][w] = 0;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) {
+        if (b0 + u < r1) {
+          store_cols<W>(h + (int64_t)(b0 + u) * E, run);
+#pragma unroll
+          for (int w = 0; w < W; ++w) run[w] += v[u][w];
+        }
+      }
+    }
+  }
+  if (active && grp == 0) {
+#pragma unroll
+    for (int w = 0; w < W; ++w) totals[col * W + w] = total[w];
+  }
+}
+
 // Run by the workgroup that arrived last, after its acquire fence: every
-// workgroup's histogram row is in ws.hist[b*E + e].  Each expert's column
-// is scanned once, in place, into the exclusive prefix over workgroups
-// (workgroup b's first rank for that expert); its total is the expert's
-// count, from which the padded scan follows.  `part` is LDS scratch of at
-// least kLayoutThreads ints.
+// workgroup's histogram row is in ws.hist[b*E + e].  The columns are scanned
+// (scan_columns), then the padded scan of the totals gives the offsets.
+// `part` is LDS scratch of at least 5 * kLayoutThreads ints.
 __device__ void finish_layout(const LayoutScratch& ws, int32_t blocks, int32_t E, int32_t align,
                               int* part, int* wave_tot, int* flags_lds,
                               int32_t* __restrict__ counts, int32_t* __restrict__ send,
                               int32_t* __restrict__ status, const RankSplit& ranks) {
   const int tid = threadIdx.x;
-  int epad = 1;
-  while (epad < E) epad <<= 1;
-  const int groups = kLayoutThreads / epad;  // threads per column, each a run of rows
-  const int col = tid & (epad - 1);
-  const int grp = tid / epad;
-  const int rows = (blocks + groups - 1) / groups;
-  const int r0 = min(blocks, grp * rows), r1 = min(blocks, r0 + rows);
-  const bool active = col < E;
-  int32_t* __restrict__ h = ws.hist;
-
   // Each workgroup's flag word is one thread's (at most kLayoutMaxBlocks <
-  // kLayoutThreads workgroups); its load is issued with pass 1's.
+  // kLayoutThreads workgroups); its load is issued before the columns'.
   static_assert(kLayoutMaxBlocks <= kLayoutThreads, "one flag word per thread");
   const int f = (tid < blocks) ? ws.flags[tid] : 0;
-  // Pass 1: this thread's partial column sum, 16 independent loads at a time.
-  // A run of at most 16 rows (every run when blocks <= 16 * groups) stays in
-  // registers for pass 2.
-  const bool fits = r1 - r0 <= 16;
-  int partial = 0;
-  int kept[16];
-  if (active && fits) {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) kept[u] = (r0 + u < r1) ? h[(int64_t)(r0 + u) * E + col] : 0;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) partial += kept[u];
-  } else if (active) {
-    for (int b0 = r0; b0 < r1; b0 += 16) {
-      int v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        v[u] = (b0 + u < r1) ? h[(int64_t)(b0 + u) * E + col] : 0;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) partial += v[u];
-    }
-  }
-  part[tid] = partial;
+  int* totals = part + 4 * kLayoutThreads;
+  if ((E & 3) == 0)
+    scan_columns<4>(ws, blocks, E, part, totals);
+  else
+    scan_columns<1>(ws, blocks, E, part, totals);
   if (f) atomicOr(flags_lds, f);
   __syncthreads();
-  int run = 0, total = 0;
-  for (int g = 0; g < groups; ++g) {
-    const int p = part[g * epad + col];
-    run += (g < grp) ? p : 0;
-    total += p;
-  }
-  // Pass 2: the exclusive prefix down the column, written over the counts.
-  if (active && fits) {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      if (r0 + u < r1) h[(int64_t)(r0 + u) * E + col] = run;
-      run += kept[u];
-    }
-  } else if (active) {
-    for (int b0 = r0; b0 < r1; b0 += 16) {
-      int v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        v[u] = (b0 + u < r1) ? h[(int64_t)(b0 + u) * E + col] : 0;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (b0 + u < r1) h[(int64_t)(b0 + u) * E + col] = run;
-        run += v[u];
-      }
-    }
-  }
-  __syncthreads();
-  if (grp == 0) part[col] = total;  // column totals (partial sums no longer needed)
-  __syncthreads();
-  write_counts_and_offsets(tid < E ? part[tid] : 0, E, align, wave_tot, counts, send, ranks);
+  write_counts_and_offsets(tid < E ? totals[tid] : 0, E, align, wave_tot, counts, send, ranks);
   if (tid == 0) {
     if (status) *status = *flags_lds;
     atomicExch(ws.arrivals, 0);  // ready for the next call
@@ -209,8 +287,10 @@ __device__ void finish_layout(const LayoutScratch& ws, int32_t blocks, int32_t E
 // SplitMix64 draw, replica = first r of the expert's range with
 // u <= thresholds[r] (TEMPO summary, section 2: probabilistic replica
 // dispatch and count gathering in one in-graph kernel).
-// Workgroups past rank_blocks read the token rows ahead instead.
-template <int R>
+// Workgroups past rank_blocks read the token rows ahead instead.  MAPPED
+// (a replica map is given) is a template parameter, so that the plain
+// ranking carries none of the mapping's code and registers.
+template <int R, bool MAPPED>
 __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     const int32_t* __restrict__ ids, int32_t n_pairs, int32_t k, int32_t E, int32_t align,
     int32_t chunk_pairs, int32_t chunks, int32_t* __restrict__ ranks_out, LayoutScratch ws,
@@ -230,7 +310,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
   __shared__ int wave_tot[kLayoutWaves];
   __shared__ int flags_lds;
   __shared__ int last_lds;
-  const bool mapped = map.offsets != nullptr;
+  constexpr bool mapped = MAPPED;
   const int32_t n_ids = mapped ? map.n_logical : E;  // valid range of the input ids
 
   const int tid = threadIdx.x;
@@ -268,10 +348,14 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
   const unsigned long long below_me = (1ull << lane) - 1ull;
   // Repeated experts within a token: when K divides the wave, every chunk's
   // 64-pair sub-rounds hold whole tokens, so a repeat shows in the expert's
-  // lane mask as a second bit among the token's K lanes.  Otherwise (and for
-  // repeats of logical experts under a replica map) the chunk's ids are
-  // staged in LDS and each token's K ids compared.
-  const bool mask_dups = !mapped && kWave % k == 0;
+  // lane mask as a second bit among the token's K lanes; under a replica map
+  // (repeats are of logical experts, which the masks no longer see) each
+  // lane compares its id with the token's earlier lanes' by cross-lane
+  // shuffles instead.  Otherwise the chunk's ids are staged in LDS and each
+  // token's K ids compared.
+  const bool whole_tokens = kWave % k == 0;
+  const bool mask_dups = !mapped && whole_tokens;
+  const bool shuffle_dups = mapped && whole_tokens;
   const unsigned long long token_lanes =
       (k >= kWave ? ~0ull : ((1ull << k) - 1ull)) << (lane - lane % k);
   for (int c = 0; c < chunks; ++c) {
@@ -286,34 +370,71 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
         e[s] = (i < end) ? ids[i] : 0;
       }
     }
-    if (!mask_dups) {
+    if (!whole_tokens) {
 #pragma unroll
       for (int s = 0; s < R; ++s) {
         const int64_t i = wbase + s * kWave + lane;
         if (i < end) chunk_ids[i - begin] = e[s];  // as given, before any replica mapping
       }
     }
+    if (shuffle_dups) {
+      // Lane pos of a token against each earlier lane of it, the R
+      // sub-rounds' shuffles of one distance issued together.
+      const int pos = lane % k;  // this pair's place in its token
+      bool valid[R];
+#pragma unroll
+      for (int s = 0; s < R; ++s) {
+        const int64_t i = wbase + s * kWave + lane;
+        valid[s] = i < end && e[s] >= 0 && e[s] < n_ids;
+      }
+      for (int d = 1; d < k; ++d) {
+        int other[R];
+#pragma unroll
+        for (int s = 0; s < R; ++s) other[s] = __shfl_up(e[s], d, kWave);
+#pragma unroll
+        for (int s = 0; s < R; ++s)
+          if (valid[s] && pos >= d && other[s] == e[s]) fl |= MOE_FLAG_DUP_ID;
+      }
+    }
 
     if (mapped) {
+      // Replica r of pair i: the first q of its expert's range (clipped to
+      // [0, E)) with u <= thresholds[q].  The R pairs' table lookups go
+      // side by side, one step of their ranges at a time, rather than one
+      // pair's whole search after another's.
+      int lo[R], hi[R], r[R];
+      uint32_t u[R];
+      int steps = 0;
+#pragma unroll
+      for (int s = 0; s < R; ++s) {
+        const int64_t i = wbase + s * kWave + lane;
+        const bool valid = i < end && e[s] >= 0 && e[s] < n_ids;
+        if (i < end && !valid) fl |= MOE_FLAG_ID_RANGE;
+        lo[s] = valid ? max(rep_off[e[s]], 0) : 0;
+        hi[s] = valid ? min(rep_off[e[s] + 1], E) : 0;
+        u[s] = (uint32_t)(splitmix64(map.seed, (uint64_t)i) >> 32);
+        r[s] = -1;
+        steps = max(steps, hi[s] - lo[s]);
+      }
+      for (int d = 0; d < steps; ++d) {
+        // Read unconditionally (the index kept in range), so that the R
+        // reads go out together.
+        uint32_t thr[R];
+#pragma unroll
+        for (int s = 0; s < R; ++s) thr[s] = rep_thr[min(lo[s] + d, E - 1)];
+#pragma unroll
+        for (int s = 0; s < R; ++s) {
+          const int q = lo[s] + d;
+          if (r[s] < 0 && q < hi[s] && u[s] <= thr[s]) r[s] = q;
+        }
+      }
 #pragma unroll
       for (int s = 0; s < R; ++s) {
         const int64_t i = wbase + s * kWave + lane;
         if (i >= end) continue;
-        int r = -1;
-        if (e[s] >= 0 && e[s] < n_ids) {
-          const uint32_t u = (uint32_t)(splitmix64(map.seed, (uint64_t)i) >> 32);
-          const int lo = rep_off[e[s]], hi = rep_off[e[s] + 1];
-          for (int q = lo; q < hi; ++q)
-            if (q >= 0 && q < E && u <= rep_thr[q]) {
-              r = q;
-              break;
-            }
-          if (r < 0) fl |= MOE_FLAG_REPLICA;
-        } else {
-          fl |= MOE_FLAG_ID_RANGE;
-        }
-        map.out[i] = r;
-        e[s] = r;  // ranked as a physical replica; -1 drops the pair
+        if (r[s] < 0 && e[s] >= 0 && e[s] < n_ids) fl |= MOE_FLAG_REPLICA;
+        map.out[i] = r[s];
+        e[s] = r[s];  // ranked as a physical replica; -1 drops the pair
       }
     }
 
@@ -343,7 +464,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
       __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
-    if (!mask_dups) fl |= duplicate_flags(chunk_ids, (int32_t)(end - begin), k, n_ids);
+    if (!whole_tokens) fl |= duplicate_flags(chunk_ids, (int32_t)(end - begin), k, n_ids);
 
     // Exclusive prefix over waves, per expert, after the earlier chunks.
     int run = 0;
@@ -500,9 +621,14 @@ void launch_rank(const LayoutPlan& plan, const int32_t* ids, int32_t k, int32_t 
                  int32_t* ranks_out, const LayoutScratch& ws, int32_t* counts, int32_t* send,
                  int32_t* status, const ReplicaMap& map, const RankSplit& ranks,
                  hipStream_t stream, const ReadAhead& ahead, int32_t ahead_blocks) {
-  launch_kernel(layout_rank_kernel<R>, plan.blocks + ahead_blocks, kLayoutThreads, stream,
-      ids, (int32_t)plan.n_pairs, k, E, align, plan.chunk_pairs, plan.chunks, ranks_out, ws,
-      counts, send, status, map, ranks, ahead, plan.blocks, ahead_blocks);
+  if (map.offsets != nullptr)
+    launch_kernel(layout_rank_kernel<R, true>, plan.blocks + ahead_blocks, kLayoutThreads,
+        stream, ids, (int32_t)plan.n_pairs, k, E, align, plan.chunk_pairs, plan.chunks,
+        ranks_out, ws, counts, send, status, map, ranks, ahead, plan.blocks, ahead_blocks);
+  else
+    launch_kernel(layout_rank_kernel<R, false>, plan.blocks + ahead_blocks, kLayoutThreads,
+        stream, ids, (int32_t)plan.n_pairs, k, E, align, plan.chunk_pairs, plan.chunks,
+        ranks_out, ws, counts, send, status, map, ranks, ahead, plan.blocks, ahead_blocks);
 }
 
 }  // namespace
