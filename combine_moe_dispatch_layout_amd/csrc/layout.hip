@@ -400,8 +400,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
     if (mapped) {
       // Replica r of pair i: the first q of its expert's range (clipped to
       // [0, E)) with u <= thresholds[q].  The R pairs' table lookups go
-      // side by side, one step of their ranges at a time, rather than one
-      // pair's whole search after another's.
+      // side by side rather than one pair's whole search after another's.
       int lo[R], hi[R], r[R];
       uint32_t u[R];
       int steps = 0;
@@ -416,9 +415,25 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
         r[s] = -1;
         steps = max(steps, hi[s] - lo[s]);
       }
-      for (int d = 0; d < steps; ++d) {
-        // Read unconditionally (the index kept in range), so that the R
-        // reads go out together.
+      // The first kFirstSteps entries of every range in one round of reads
+      // (read unconditionally, the index kept in range, so that they all go
+      // out together); longer ranges continue one step at a time.
+      constexpr int kFirstSteps = 4;
+      {
+        uint32_t thr[R][kFirstSteps];
+#pragma unroll
+        for (int s = 0; s < R; ++s)
+#pragma unroll
+          for (int d = 0; d < kFirstSteps; ++d) thr[s][d] = rep_thr[min(lo[s] + d, E - 1)];
+#pragma unroll
+        for (int s = 0; s < R; ++s)
+#pragma unroll
+          for (int d = 0; d < kFirstSteps; ++d) {
+            const int q = lo[s] + d;
+            if (r[s] < 0 && q < hi[s] && u[s] <= thr[s][d]) r[s] = q;
+          }
+      }
+      for (int d = kFirstSteps; d < steps; ++d) {
         uint32_t thr[R];
 #pragma unroll
         for (int s = 0; s < R; ++s) thr[s] = rep_thr[min(lo[s] + d, E - 1)];

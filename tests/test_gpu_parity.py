@@ -853,10 +853,12 @@ def test_maximum_row_two_launch_fused():
 
 def test_layout_many_workgroups_every_expert_count():
     """Tens to 256 ranking workgroups with E from 1 to 512, so the last
-    workgroup's column scan runs with 512 down to 1 threads per column."""
+    workgroup's column scan runs with 512 down to 1 threads per column, on
+    4-column (16-byte) and single columns (E not a multiple of 4), with its
+    rows kept in registers between the passes or read again."""
     rng = np.random.default_rng(103)
     for bs, e, k in [(200000, 1, 1), (60000, 3, 2), (100000, 8, 2), (30000, 100, 8),
-                     (40000, 300, 4), (30000, 512, 16)]:
+                     (40000, 300, 4), (30000, 512, 16), (100000, 511, 3), (60000, 37, 5)]:
         assert_layout_equal(random_ids(rng, bs, e, k), e, 128)
 
 
