@@ -320,8 +320,12 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
   const int64_t bbegin = (int64_t)blockIdx.x * ppb;
   const int64_t bend = min((int64_t)n_pairs, bbegin + ppb);
 
-  // The first chunk's id loads are issued before the LDS set-up.
+  // The first chunk's id loads are issued before the LDS set-up, and under
+  // a replica map so are the tables' loads (at most n_ids + 1 <= 513
+  // offsets and E <= 512 thresholds: two and one per thread) and the first
+  // chunk's draws, which depend on the pair index only.
   int e[R];
+  uint32_t u0[R];
   {
     const int64_t end = min(bend, bbegin + chunk_pairs);
     const int64_t wbase = bbegin + wave * (kWave * R);
@@ -331,6 +335,19 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
       e[s] = (i < end) ? ids[i] : 0;
     }
   }
+  static_assert(kMaxExperts + 1 <= 2 * kLayoutThreads && kMaxExperts <= kLayoutThreads,
+                "replica tables: two offsets and one threshold per thread");
+  int off_a = 0, off_b = 0;
+  uint32_t thr_a = 0;
+  if (mapped) {
+    if (tid <= n_ids) off_a = map.offsets[tid];
+    if (tid + kLayoutThreads <= n_ids) off_b = map.offsets[tid + kLayoutThreads];
+    if (tid < E) thr_a = map.thresholds[tid];
+    const int64_t wbase = bbegin + wave * (kWave * R);
+#pragma unroll
+    for (int s = 0; s < R; ++s)
+      u0[s] = (uint32_t)(splitmix64(map.seed, (uint64_t)(wbase + s * kWave + lane)) >> 32);
+  }
 
   for (int j = tid; j < kLayoutWaves * kMaxExperts; j += kLayoutThreads) {
     (&mask[0][0])[j] = 0ull;
@@ -339,8 +356,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
   for (int j = tid; j < kMaxExperts; j += kLayoutThreads) blk_run[j] = 0;
   if (tid == 0) flags_lds = 0;
   if (mapped) {
-    for (int j = tid; j <= n_ids; j += kLayoutThreads) rep_off[j] = map.offsets[j];
-    for (int j = tid; j < E; j += kLayoutThreads) rep_thr[j] = map.thresholds[j];
+    if (tid <= n_ids) rep_off[tid] = off_a;
+    if (tid + kLayoutThreads <= n_ids) rep_off[tid + kLayoutThreads] = off_b;
+    if (tid < E) rep_thr[tid] = thr_a;
   }
   int fl = 0;
   __syncthreads();
@@ -411,7 +429,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
         if (i < end && !valid) fl |= MOE_FLAG_ID_RANGE;
         lo[s] = valid ? max(rep_off[e[s]], 0) : 0;
         hi[s] = valid ? min(rep_off[e[s] + 1], E) : 0;
-        u[s] = (uint32_t)(splitmix64(map.seed, (uint64_t)i) >> 32);
+        u[s] = c == 0 ? u0[s] : (uint32_t)(splitmix64(map.seed, (uint64_t)i) >> 32);
         r[s] = -1;
         steps = max(steps, hi[s] - lo[s]);
       }
