@@ -625,13 +625,21 @@ def test_replicated_layout_matches_oracle(bs, e, k, max_rep, seed):
         assert_replicated_equal(ids, e, off, thr, seed, align)
 
 
-def test_replicated_layout_flags():
-    rng = np.random.default_rng(3)
-    e, k, bs = 16, 4, 3000
+@pytest.mark.parametrize("bs,k", [(3000, 4),    # several workgroups, K divides the wave
+                                  (3000, 3),    # several workgroups, ids staged for repeats
+                                  (200, 8),     # one workgroup, K divides the wave
+                                  (300, 5)])    # one workgroup, ids staged
+def test_replicated_layout_flags(bs, k):
+    """Out-of-range logical ids, logical experts repeated within a token
+    (neighbouring and first-to-last lanes), and an expert whose replicas
+    take almost no draw: everything, flags included, as the oracle."""
+    rng = np.random.default_rng(3 + k)
+    e = 16
     off, thr = random_replica_table(rng, e, 3)
     ids = random_ids(rng, bs, e, k)
     ids[::11, 0] = e + 3                     # out-of-range logical ids
-    ids[::13, 2] = ids[::13, 1]              # repeated experts
+    ids[::13, 2 % k] = ids[::13, 1 % k]      # repeated experts, neighbouring lanes
+    ids[5::17, k - 1] = ids[5::17, 0]        # and the token's first and last lanes
     thr = thr.copy()
     thr[off[5]:off[6]] = 0                   # expert 5 can only map when u == 0
     rep, s, r, lay, grep = assert_replicated_equal(ids, e, off, thr, 9, 128)
